@@ -1,0 +1,92 @@
+// dequantize.hip - codes * scale back to binary32 or bfloat16 (gather side of
+// the QWZ all-gather).
+//
+// Page "Quantized LLM Training at Scale with ZeRO++", section "The Three
+// Pillars of ZeRO++", pillar 1 (QWZ): weights travel as 8-bit values; the
+// receiver needs the 16-bit layer weights back to compute with. Each value
+// is the binary32 product code * s_b; bf16 output rounds it to nearest-even.
+//
+// A lane owns 8 consecutive elements per segment: 8 (int8) or 4 (int4) code
+// bytes in, 16 (bf16) or 32 (fp32) bytes out, all contiguous across the
+// wave. The lane's block scale is a per-lane load (lanes of one block hit
+// the same address).
+#include "zpp_device.h"
+#include "zpp_launch.h"
+
+namespace zpp {
+namespace {
+
+constexpr int kE = 8;              // elements per lane per segment
+constexpr int kSeg = kWave * kE;   // 512
+constexpr int kU = 4;              // segments per tile
+constexpr int kTile = kU * kSeg;
+
+template <int BITS, bool F32OUT>
+__global__ __launch_bounds__(kBlockThreads) void dequantize_kernel(const uint8_t *__restrict__ codes,
+                                                                   const float *__restrict__ scales, int64_t numel,
+                                                                   int log2b, uint8_t *__restrict__ y) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t wave = static_cast<int64_t>(blockIdx.x) * (kBlockThreads / kWave) + (threadIdx.x / kWave);
+    const int64_t n_waves = static_cast<int64_t>(gridDim.x) * (kBlockThreads / kWave);
+
+    for (int64_t t0 = wave * kTile; t0 < numel; t0 += n_waves * kTile) {
+        uint32_t w[kU][2];
+        float s[kU];
+        bool ok[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t e0 = t0 + static_cast<int64_t>(u) * kSeg + lane * kE;
+            ok[u] = e0 < numel;
+            const int64_t e = ok[u] ? e0 : 0;
+            if constexpr (BITS == 8) {
+                const u32x2 c = ld<u32x2>(codes + e);
+                w[u][0] = c[0];
+                w[u][1] = c[1];
+            } else {
+                w[u][0] = ld<uint32_t>(codes + e / 2);
+                w[u][1] = 0;
+            }
+            s[u] = scales[e >> log2b];
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            if (!ok[u]) continue;
+            const int64_t e0 = t0 + static_cast<int64_t>(u) * kSeg + lane * kE;
+            float f[kE];
+#pragma unroll
+            for (int i = 0; i < kE; ++i) {
+                const int32_t q = (BITS == 8) ? code_at<8>(w[u][i / 4], i % 4) : code_at<4>(w[u][0], i);
+                f[i] = static_cast<float>(q) * s[u];
+            }
+            if constexpr (F32OUT) {
+                uint8_t *dst = y + e0 * 4;
+                st<u32x4>(dst, u32x4{as_u(f[0]), as_u(f[1]), as_u(f[2]), as_u(f[3])});
+                st<u32x4>(dst + 16, u32x4{as_u(f[4]), as_u(f[5]), as_u(f[6]), as_u(f[7])});
+            } else {
+                st<u32x4>(y + e0 * 2, u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                                            pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])});
+            }
+        }
+    }
+}
+
+template <int BITS, bool F32OUT>
+hipError_t launch(const void *codes, const float *scales, int64_t numel, int log2b, void *y, hipStream_t stream) {
+    const int64_t tiles = (numel + kTile - 1) / kTile;
+    dequantize_kernel<BITS, F32OUT><<<stream_grid(tiles), kBlockThreads, 0, stream>>>(
+        static_cast<const uint8_t *>(codes), scales, numel, log2b, static_cast<uint8_t *>(y));
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_dequantize(const void *codes, const float *scales, int bits, int64_t numel, int log2b, void *y,
+                             bool f32_out, hipStream_t stream) {
+    if (bits == 8)
+        return f32_out ? launch<8, true>(codes, scales, numel, log2b, y, stream)
+                       : launch<8, false>(codes, scales, numel, log2b, y, stream);
+    return f32_out ? launch<4, true>(codes, scales, numel, log2b, y, stream)
+                   : launch<4, false>(codes, scales, numel, log2b, y, stream);
+}
+
+}  // namespace zpp

@@ -1,0 +1,162 @@
+// quantize.hip - per-block symmetric absmax quantization (QWZ 8-bit weights,
+// QGZ one-shot 4-bit gradients).
+//
+// Page "Quantized LLM Training at Scale with ZeRO++", section "The Three
+// Pillars of ZeRO++": pillar 1 (QWZ) quantizes the weight tensor chunk by
+// chunk to 8 bits before the forward all-gather; pillar 3 (QGZ) quantizes
+// each GPU's gradient once, to 4 bits (a quarter of the 16-bit volume),
+// before its all-to-all.
+//
+// Layout of the work. A lane owns one 16-byte input vector per segment
+// (8 bf16 or 4 fp32 elements); a wave's 64 lanes cover a contiguous segment
+// of 512 (bf16) or 256 (fp32) elements, so every load instruction reads one
+// contiguous kilobyte and every code store writes one contiguous run. A
+// block of B elements spans L = B / 8 lanes (bf16) inside a segment, or
+// several whole segments when B is larger than a segment. Each wave works on
+// tiles of U segments (all U loads issued before any use) in a grid-stride
+// loop. The block maximum is reduced across its lanes with DPP / permlane
+// swaps; the lane at the head of each block stores its scale.
+#include "zpp_device.h"
+#include "zpp_launch.h"
+
+namespace zpp {
+namespace {
+
+template <int BITS, int LOG2B, bool F32IN>
+struct QuantGeom {
+    static constexpr int B = 1 << LOG2B;
+    static constexpr int IB = F32IN ? 4 : 2;            // input bytes per element
+    static constexpr int E = 16 / IB;                   // elements per lane per segment
+    static constexpr int SEG = kWave * E;               // elements per wave segment
+    static constexpr int SPB = B > SEG ? B / SEG : 1;   // segments per block
+    static constexpr int L = B >= SEG ? kWave : B / E;  // lanes per block within a segment
+    static constexpr int U = SPB > 4 ? SPB : 4;         // segments per tile
+    static constexpr int NB = U / SPB;                  // scale slots per lane per tile
+    static constexpr int TILE = U * SEG;
+    static constexpr int CB = E * BITS / 8;             // code bytes per lane per segment
+    static constexpr int QMAX = BITS == 8 ? 127 : 7;
+};
+
+template <int BITS, int LOG2B, bool F32IN>
+__global__ __launch_bounds__(kBlockThreads) void quantize_kernel(const uint8_t *__restrict__ x, int64_t numel,
+                                                                 uint8_t *__restrict__ codes,
+                                                                 float *__restrict__ scales) {
+    using G = QuantGeom<BITS, LOG2B, F32IN>;
+    constexpr int E = G::E, U = G::U, SPB = G::SPB, NB = G::NB;
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t wave = static_cast<int64_t>(blockIdx.x) * (kBlockThreads / kWave) + (threadIdx.x / kWave);
+    const int64_t n_waves = static_cast<int64_t>(gridDim.x) * (kBlockThreads / kWave);
+
+    for (int64_t t0 = wave * G::TILE; t0 < numel; t0 += n_waves * G::TILE) {
+        float v[U][E];
+        bool ok[U];
+        // Issue every load of the tile first. Out-of-range lanes (only in the
+        // last tile, and only for whole blocks since numel % B == 0) read
+        // element 0 instead and are masked out afterwards.
+        u32x4 raw[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t e0 = t0 + static_cast<int64_t>(u) * G::SEG + lane * E;
+            ok[u] = e0 < numel;
+            raw[u] = ld<u32x4>(x + (ok[u] ? e0 : 0) * G::IB);
+        }
+        uint32_t m[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if constexpr (F32IN) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[u][i] = ok[u] ? as_f(raw[u][i]) : 0.0f;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t w = ok[u] ? raw[u][i] : 0u;
+                    v[u][2 * i] = bf16_lo(w);
+                    v[u][2 * i + 1] = bf16_hi(w);
+                }
+            }
+            uint32_t mx = 0;
+#pragma unroll
+            for (int i = 0; i < E; ++i) mx = max(mx, as_u(v[u][i]) & 0x7FFFFFFFu);
+            m[u] = mx;
+        }
+
+        // Block absmax -> scale, one per block (per segment when SPB == 1).
+        float s[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            uint32_t mx = 0;
+#pragma unroll
+            for (int k = 0; k < SPB; ++k) mx = max(mx, m[b * SPB + k]);
+            mx = group_max_u32<G::L>(mx);
+            s[b] = as_f(mx) / static_cast<float>(G::QMAX);  // correctly rounded division
+        }
+
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t e0 = t0 + static_cast<int64_t>(u) * G::SEG + lane * E;
+            int32_t q[E];
+            quantize_values<E, G::QMAX>(v[u], s[u / SPB], q);
+            if (!ok[u]) continue;
+            uint8_t *dst = codes + e0 * BITS / 8;
+            if constexpr (BITS == 8) {
+                if constexpr (E == 8)
+                    st<u32x2>(dst, u32x2{pack_i8x4(q[0], q[1], q[2], q[3]), pack_i8x4(q[4], q[5], q[6], q[7])});
+                else
+                    st<uint32_t>(dst, pack_i8x4(q[0], q[1], q[2], q[3]));
+            } else {
+                if constexpr (E == 8) {
+                    st<uint32_t>(dst, pack_i4x8(q));
+                } else {
+                    const uint32_t w = (static_cast<uint32_t>(q[0]) & 0xF) | ((static_cast<uint32_t>(q[1]) & 0xF) << 4) |
+                                       ((static_cast<uint32_t>(q[2]) & 0xF) << 8) |
+                                       ((static_cast<uint32_t>(q[3]) & 0xF) << 12);
+                    st<uint16_t>(dst, static_cast<uint16_t>(w));
+                }
+            }
+            if constexpr (SPB == 1) {
+                if ((lane & (G::L - 1)) == 0) scales[e0 >> LOG2B] = s[u];
+            } else {
+                if (lane == 0 && (u % SPB) == 0) scales[e0 >> LOG2B] = s[u / SPB];
+            }
+        }
+    }
+}
+
+template <int BITS, int LOG2B, bool F32IN>
+hipError_t launch(const void *x, int64_t numel, void *codes, float *scales, hipStream_t stream) {
+    using G = QuantGeom<BITS, LOG2B, F32IN>;
+    const int64_t tiles = (numel + G::TILE - 1) / G::TILE;
+    const int grid = stream_grid(tiles);
+    quantize_kernel<BITS, LOG2B, F32IN><<<grid, kBlockThreads, 0, stream>>>(
+        static_cast<const uint8_t *>(x), numel, static_cast<uint8_t *>(codes), scales);
+    return hipGetLastError();
+}
+
+template <int BITS, bool F32IN>
+hipError_t by_block(int log2b, const void *x, int64_t numel, void *codes, float *scales, hipStream_t st) {
+    switch (log2b) {
+    case 5: return launch<BITS, 5, F32IN>(x, numel, codes, scales, st);
+    case 6: return launch<BITS, 6, F32IN>(x, numel, codes, scales, st);
+    case 7: return launch<BITS, 7, F32IN>(x, numel, codes, scales, st);
+    case 8: return launch<BITS, 8, F32IN>(x, numel, codes, scales, st);
+    case 9: return launch<BITS, 9, F32IN>(x, numel, codes, scales, st);
+    case 10: return launch<BITS, 10, F32IN>(x, numel, codes, scales, st);
+    case 11: return launch<BITS, 11, F32IN>(x, numel, codes, scales, st);
+    case 12: return launch<BITS, 12, F32IN>(x, numel, codes, scales, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const void *x, bool f32_in, int64_t numel, int log2b, int bits, void *codes,
+                           float *scales, hipStream_t stream) {
+    if (bits == 8)
+        return f32_in ? by_block<8, true>(log2b, x, numel, codes, scales, stream)
+                      : by_block<8, false>(log2b, x, numel, codes, scales, stream);
+    return f32_in ? by_block<4, true>(log2b, x, numel, codes, scales, stream)
+                  : by_block<4, false>(log2b, x, numel, codes, scales, stream);
+}
+
+}  // namespace zpp

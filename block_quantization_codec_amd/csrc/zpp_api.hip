@@ -1,0 +1,228 @@
+// zpp_api.hip - the C ABI declared in include/zpp.h.
+//
+// Every entry point validates its arguments on the host before touching the
+// GPU: pure argument checks first (null pointers, sizes, block, bit widths,
+// alignment, overlapping outputs), then checks with the HIP runtime that
+// every pointer is memory the GPU can address and that each buffer's whole
+// byte range lies inside its allocation. Only then is a kernel launched on
+// the caller's stream. Any failure returns a status code with nothing
+// launched and every output untouched.
+#include <atomic>
+#include <cstdint>
+
+#include "../../include/zpp.h"
+#include "zpp_device.h"
+#include "zpp_launch.h"
+
+namespace zpp {
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+
+int device_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    int cus = g_cus[dev].load(std::memory_order_relaxed);
+    if (cus <= 0) {
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+            (void)hipGetLastError();
+            cus = 256;
+        }
+        g_cus[dev].store(cus, std::memory_order_relaxed);
+    }
+    return cus;
+}
+
+}  // namespace
+
+int stream_grid(int64_t tiles) {
+    // 4 waves per workgroup, each wave one tile per iteration; cap at 8
+    // resident workgroups (32 waves) per CU and let the grid-stride loop
+    // cover the rest.
+    const int64_t want = (tiles + (kBlockThreads / kWave) - 1) / (kBlockThreads / kWave);
+    const int64_t cap = static_cast<int64_t>(device_cus()) * 8;
+    const int64_t g = want < cap ? want : cap;
+    return static_cast<int>(g < 1 ? 1 : g);
+}
+
+}  // namespace zpp
+
+namespace {
+
+struct Range {
+    const void *p;
+    int64_t bytes;
+};
+
+bool is_pow2_block(int32_t b) { return b >= ZPP_MIN_BLOCK && b <= ZPP_MAX_BLOCK && (b & (b - 1)) == 0; }
+
+int log2_of(int32_t b) {
+    int l = 0;
+    while ((1 << l) < b) ++l;
+    return l;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlap(Range a, Range b) {
+    if (a.bytes <= 0 || b.bytes <= 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + static_cast<uintptr_t>(b.bytes) && b0 < a0 + static_cast<uintptr_t>(a.bytes);
+}
+
+// The pointer must be device-addressable and [p, p + bytes) must lie in one allocation.
+zpp_status check_device_range(Range r) {
+    if (r.bytes <= 0) return ZPP_OK;
+    hipPointerAttribute_t attr;
+    hipError_t e = hipPointerGetAttributes(&attr, r.p);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return ZPP_ERR_POINTER;
+    }
+    if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged && attr.type != hipMemoryTypeHost &&
+        attr.type != hipMemoryTypeUnified)
+        return ZPP_ERR_POINTER;
+    if (attr.type == hipMemoryTypeHost && attr.devicePointer == nullptr) return ZPP_ERR_POINTER;
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    e = hipMemGetAddressRange(&base, &size, const_cast<void *>(r.p));
+    if (e == hipSuccess && base != nullptr && size > 0) {
+        const uintptr_t b0 = reinterpret_cast<uintptr_t>(base);
+        const uintptr_t p0 = reinterpret_cast<uintptr_t>(r.p);
+        if (p0 < b0 || p0 + static_cast<uintptr_t>(r.bytes) > b0 + size) return ZPP_ERR_ARG;
+    } else {
+        (void)hipGetLastError();
+    }
+    return ZPP_OK;
+}
+
+template <size_t N>
+zpp_status check_all(const Range (&rs)[N]) {
+    for (const Range &r : rs) {
+        const zpp_status s = check_device_range(r);
+        if (s != ZPP_OK) return s;
+    }
+    return ZPP_OK;
+}
+
+zpp_status launched(hipError_t e) {
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return ZPP_ERR_LAUNCH;
+    }
+    return ZPP_OK;
+}
+
+int64_t code_bytes(int64_t numel, int32_t bits) { return numel * bits / 8; }
+
+}  // namespace
+
+extern "C" {
+
+zpp_status zpp_quantize_blocks(const void *x, zpp_dtype x_dtype, int64_t numel, int32_t block, int32_t bits,
+                               void *codes, float *scales, void *stream) {
+    if (x_dtype != ZPP_BF16 && x_dtype != ZPP_FP32) return ZPP_ERR_ARG;
+    if (bits != 8 && bits != 4) return ZPP_ERR_ARG;
+    if (!is_pow2_block(block) || numel < 0 || numel % block != 0) return ZPP_ERR_ARG;
+    if (numel == 0) return ZPP_OK;
+    if (!x || !codes || !scales) return ZPP_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4)) return ZPP_ERR_ALIGN;
+    const int64_t in_bytes = numel * (x_dtype == ZPP_BF16 ? 2 : 4);
+    const Range in{x, in_bytes}, oc{codes, code_bytes(numel, bits)}, os{scales, 4 * (numel / block)};
+    if (overlap(oc, in) || overlap(os, in) || overlap(oc, os)) return ZPP_ERR_OVERLAP;
+    const Range all[] = {in, oc, os};
+    if (zpp_status s = check_all(all); s != ZPP_OK) return s;
+    return launched(zpp::launch_quantize(x, x_dtype == ZPP_FP32, numel, log2_of(block), bits, codes, scales,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+zpp_status zpp_dequantize_blocks(const void *codes, const float *scales, int32_t bits, int64_t numel, int32_t block,
+                                 void *y, zpp_dtype y_dtype, void *stream) {
+    if (y_dtype != ZPP_BF16 && y_dtype != ZPP_FP32) return ZPP_ERR_ARG;
+    if (bits != 8 && bits != 4) return ZPP_ERR_ARG;
+    if (!is_pow2_block(block) || numel < 0 || numel % block != 0) return ZPP_ERR_ARG;
+    if (numel == 0) return ZPP_OK;
+    if (!codes || !scales || !y) return ZPP_ERR_NULL;
+    if (!aligned(codes, 16) || !aligned(y, 16) || !aligned(scales, 4)) return ZPP_ERR_ALIGN;
+    const Range ic{codes, code_bytes(numel, bits)}, is{scales, 4 * (numel / block)},
+        oy{y, numel * (y_dtype == ZPP_BF16 ? 2 : 4)};
+    if (overlap(oy, ic) || overlap(oy, is)) return ZPP_ERR_OVERLAP;
+    const Range all[] = {ic, is, oy};
+    if (zpp_status s = check_all(all); s != ZPP_OK) return s;
+    return launched(zpp::launch_dequantize(codes, scales, bits, numel, log2_of(block), y, y_dtype == ZPP_FP32,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+zpp_status zpp_reorder_slices(const void *in, void *out, int64_t slice_bytes, int32_t n_nodes,
+                              int32_t gpus_per_node, void *stream) {
+    if (n_nodes < 1 || gpus_per_node < 1 || slice_bytes < 0) return ZPP_ERR_ARG;
+    if (static_cast<int64_t>(n_nodes) * gpus_per_node > 65535) return ZPP_ERR_ARG;
+    const int64_t n = static_cast<int64_t>(n_nodes) * gpus_per_node;
+    if (slice_bytes > INT64_MAX / n) return ZPP_ERR_ARG;
+    if (slice_bytes == 0) return ZPP_OK;
+    if (!in || !out) return ZPP_ERR_NULL;
+    const Range ri{in, slice_bytes * n}, ro{out, slice_bytes * n};
+    if (overlap(ri, ro)) return ZPP_ERR_OVERLAP;
+    const Range all[] = {ri, ro};
+    if (zpp_status s = check_all(all); s != ZPP_OK) return s;
+    return launched(zpp::launch_reorder(in, out, slice_bytes, n_nodes, gpus_per_node,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+zpp_status zpp_dequant_reduce_requant(const void *codes_in, int64_t codes_stride_bytes, const float *scales_in,
+                                      int64_t scales_stride, int32_t n_inputs, int32_t bits_in, int64_t numel,
+                                      int32_t block, void *codes_out, float *scales_out, int32_t bits_out,
+                                      float *sum_out, void *stream) {
+    if (bits_in != 8 && bits_in != 4) return ZPP_ERR_ARG;
+    if (bits_out != 0 && bits_out != 8 && bits_out != 4) return ZPP_ERR_ARG;
+    if (!is_pow2_block(block) || numel < 0 || numel % block != 0) return ZPP_ERR_ARG;
+    if (n_inputs < 1 || n_inputs > ZPP_MAX_INPUTS) return ZPP_ERR_ARG;
+    if (codes_stride_bytes < 0 || scales_stride < 0) return ZPP_ERR_ARG;
+    if (bits_out == 0 && (codes_out || scales_out)) return ZPP_ERR_ARG;
+    if (bits_out == 0 && !sum_out) return ZPP_ERR_ARG;
+    if (numel == 0) return ZPP_OK;
+    if (!codes_in || !scales_in) return ZPP_ERR_NULL;
+    if (bits_out != 0 && (!codes_out || !scales_out)) return ZPP_ERR_NULL;
+    if (!aligned(codes_in, 16) || (codes_stride_bytes & 15) != 0 || !aligned(scales_in, 4)) return ZPP_ERR_ALIGN;
+    if (codes_out && !aligned(codes_out, 16)) return ZPP_ERR_ALIGN;
+    if (scales_out && !aligned(scales_out, 4)) return ZPP_ERR_ALIGN;
+    if (sum_out && !aligned(sum_out, 16)) return ZPP_ERR_ALIGN;
+    const int64_t nblk = numel / block;
+    const Range ic{codes_in, (n_inputs - 1) * codes_stride_bytes + code_bytes(numel, bits_in)},
+        is{scales_in, 4 * ((n_inputs - 1) * scales_stride + nblk)},
+        oc{codes_out, bits_out ? code_bytes(numel, bits_out) : 0}, os{scales_out, bits_out ? 4 * nblk : 0},
+        ou{sum_out, sum_out ? 4 * numel : 0};
+    const Range outs[] = {oc, os, ou};
+    for (const Range &o : outs) {
+        if (overlap(o, ic) || overlap(o, is)) return ZPP_ERR_OVERLAP;
+    }
+    if (overlap(oc, os) || overlap(oc, ou) || overlap(os, ou)) return ZPP_ERR_OVERLAP;
+    const Range all[] = {ic, is, oc, os, ou};
+    if (zpp_status s = check_all(all); s != ZPP_OK) return s;
+    return launched(zpp::launch_drr(codes_in, codes_stride_bytes, scales_in, scales_stride, n_inputs, bits_in, numel,
+                                    log2_of(block), codes_out, scales_out, bits_out, sum_out,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+const char *zpp_status_string(zpp_status status) {
+    switch (status) {
+    case ZPP_OK: return "ZPP_OK";
+    case ZPP_ERR_NULL: return "ZPP_ERR_NULL: a required pointer is NULL";
+    case ZPP_ERR_ARG: return "ZPP_ERR_ARG: invalid size, block, bit width, count, stride or buffer range";
+    case ZPP_ERR_ALIGN: return "ZPP_ERR_ALIGN: pointer or stride misaligned";
+    case ZPP_ERR_UNSUPPORTED: return "ZPP_ERR_UNSUPPORTED: combination not implemented";
+    case ZPP_ERR_OVERLAP: return "ZPP_ERR_OVERLAP: an output overlaps an input or another output";
+    case ZPP_ERR_POINTER: return "ZPP_ERR_POINTER: pointer is not GPU-addressable memory";
+    case ZPP_ERR_LAUNCH: return "ZPP_ERR_LAUNCH: the HIP runtime rejected the kernel launch";
+    }
+    return "unknown zpp_status";
+}
+
+int32_t zpp_abi_version(void) { return ZPP_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,152 @@
+"""The C-ABI library on the host: it loads, exports every entry point that
+include/zpp.h declares, and rejects invalid arguments before any GPU work.
+
+No kernel is launched here (these run on machines without a GPU): every
+argument case below fails in the library's pure host-side checks, which run
+before it makes any HIP call.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "zpp.h")
+
+
+@pytest.fixture(scope="module")
+def z():
+    from block_quantization_codec_amd import _build
+
+    if _build.stale():
+        _build.build()
+    import block_quantization_codec_amd as z
+
+    return z
+
+
+def declared_functions() -> list[str]:
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(zpp_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_codec_calls():
+    names = declared_functions()
+    for n in ("zpp_quantize_blocks", "zpp_dequantize_blocks", "zpp_reorder_slices",
+              "zpp_dequant_reduce_requant"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(z):
+    lib = ctypes.CDLL(z.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", z.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r" T (zpp_[a-z0-9_]+)$", out, flags=re.M))
+    assert exported == set(declared_functions())
+    assert set(z.EXPORTED) == exported
+
+
+def test_abi_version_and_status_strings(z):
+    assert z.zpp_abi_version() == 1
+    for s in range(0, 8):
+        assert z.zpp_status_string(s).startswith("ZPP_")
+    assert z.zpp_status_string(99) == "unknown zpp_status"
+
+
+# Fake device addresses: never dereferenced, because each case fails in the
+# pure argument checks that precede every HIP call.
+A = 1 << 40  # 16-byte aligned
+
+
+def test_quantize_argument_errors(z):
+    L = z.library()
+    q = L.zpp_quantize_blocks
+    assert q(A, 3, 256, 256, 8, A + 4096, A + 8192, None) == z.ZPP_ERR_ARG          # dtype
+    assert q(A, 1, 256, 256, 6, A + 4096, A + 8192, None) == z.ZPP_ERR_ARG          # bits
+    assert q(A, 1, 256, 100, 8, A + 4096, A + 8192, None) == z.ZPP_ERR_ARG          # block not pow2
+    assert q(A, 1, 256, 16, 8, A + 4096, A + 8192, None) == z.ZPP_ERR_ARG           # block < 32
+    assert q(A, 1, 16384, 8192, 8, A + 65536, A + 131072, None) == z.ZPP_ERR_ARG    # block > 4096
+    assert q(A, 1, 300, 256, 8, A + 4096, A + 8192, None) == z.ZPP_ERR_ARG          # numel % block
+    assert q(A, 1, -256, 256, 8, A + 4096, A + 8192, None) == z.ZPP_ERR_ARG         # negative
+    assert q(None, 1, 256, 256, 8, A + 4096, A + 8192, None) == z.ZPP_ERR_NULL
+    assert q(A, 1, 256, 256, 8, None, A + 8192, None) == z.ZPP_ERR_NULL
+    assert q(A + 2, 1, 256, 256, 8, A + 4096, A + 8192, None) == z.ZPP_ERR_ALIGN
+    assert q(A, 1, 256, 256, 8, A + 4100, A + 8192, None) == z.ZPP_ERR_ALIGN
+    assert q(A, 1, 256, 256, 8, A + 4096, A + 8194, None) == z.ZPP_ERR_ALIGN
+    assert q(A, 1, 256, 256, 8, A + 256, A + 8192, None) == z.ZPP_ERR_OVERLAP       # codes in x
+    assert q(A, 1, 256, 256, 8, A + 4096, A + 4096 + 128, None) == z.ZPP_ERR_OVERLAP  # scales in codes
+    assert q(None, 1, 0, 256, 8, None, None, None) == z.ZPP_OK                        # empty
+
+
+def test_dequantize_argument_errors(z):
+    d = z.library().zpp_dequantize_blocks
+    assert d(A, A + 4096, 8, 256, 256, A + 8192, 0, None) == z.ZPP_ERR_ARG          # dtype
+    assert d(A, A + 4096, 5, 256, 256, A + 8192, 1, None) == z.ZPP_ERR_ARG          # bits
+    assert d(A, A + 4096, 8, 257, 256, A + 8192, 1, None) == z.ZPP_ERR_ARG
+    assert d(A, None, 8, 256, 256, A + 8192, 1, None) == z.ZPP_ERR_NULL
+    assert d(A + 8, A + 4096, 8, 256, 256, A + 8192, 1, None) == z.ZPP_ERR_ALIGN
+    assert d(A, A + 4098, 8, 256, 256, A + 8192, 1, None) == z.ZPP_ERR_ALIGN
+    assert d(A, A + 4096, 8, 256, 256, A + 64, 1, None) == z.ZPP_ERR_OVERLAP         # y over codes
+    assert d(None, None, 8, 0, 256, None, 1, None) == z.ZPP_OK
+
+
+def test_reorder_argument_errors(z):
+    r = z.library().zpp_reorder_slices
+    assert r(A, A + (1 << 20), 100, 0, 4, None) == z.ZPP_ERR_ARG
+    assert r(A, A + (1 << 20), 100, 2, 0, None) == z.ZPP_ERR_ARG
+    assert r(A, A + (1 << 20), -1, 2, 4, None) == z.ZPP_ERR_ARG
+    assert r(A, A + (1 << 20), 100, 256, 256, None) == z.ZPP_ERR_ARG                 # > 65535 slices
+    assert r(None, A, 100, 2, 4, None) == z.ZPP_ERR_NULL
+    assert r(A, A + 400, 100, 2, 4, None) == z.ZPP_ERR_OVERLAP
+    assert r(None, None, 0, 2, 4, None) == z.ZPP_OK
+
+
+def test_drr_argument_errors(z):
+    f = z.library().zpp_dequant_reduce_requant
+    C, S, O, OS, U = A, A + (1 << 24), A + (1 << 25), A + (1 << 26), A + (1 << 27)
+    ok = dict(ci=C, cs=1 << 16, si=S, ss=1 << 10, R=4, bi=4, n=1 << 12, B=256, co=O, so=OS, bo=4, su=U)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["ci"], a["cs"], a["si"], a["ss"], a["R"], a["bi"], a["n"], a["B"], a["co"], a["so"],
+                 a["bo"], a["su"], None)
+
+    assert call(bi=2) == z.ZPP_ERR_ARG
+    assert call(bo=2) == z.ZPP_ERR_ARG
+    assert call(R=0) == z.ZPP_ERR_ARG
+    assert call(R=5000) == z.ZPP_ERR_ARG
+    assert call(n=300) == z.ZPP_ERR_ARG
+    assert call(cs=-16) == z.ZPP_ERR_ARG
+    assert call(bo=0, co=None, so=None, su=None) == z.ZPP_ERR_ARG                    # no output
+    assert call(bo=0) == z.ZPP_ERR_ARG                                                 # codes_out without bits
+    assert call(ci=None) == z.ZPP_ERR_NULL
+    assert call(so=None) == z.ZPP_ERR_NULL
+    assert call(cs=8) == z.ZPP_ERR_ALIGN
+    assert call(ci=C + 4) == z.ZPP_ERR_ALIGN
+    assert call(su=U + 4) == z.ZPP_ERR_ALIGN
+    assert call(co=C + 64) == z.ZPP_ERR_OVERLAP                                        # output in input
+    assert call(so=O + 16) == z.ZPP_ERR_OVERLAP                                        # outputs overlap
+    assert call(n=0) == z.ZPP_OK
+
+
+def test_oracle_and_library_share_no_code():
+    """The product sources never mention the oracle, and the oracle never the product."""
+    pkg = os.path.join(ROOT, "block_quantization_codec_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert "oracle" not in text.lower(), fn
+    for fn in os.listdir(os.path.join(ROOT, "oracle")):
+        if fn.endswith((".py", ".c", ".h")):
+            text = open(os.path.join(ROOT, "oracle", fn)).read()
+            assert not re.search(r"^\s*(import|from)\s+block_quantization_codec_amd", text, re.M), fn
+            assert not re.search(r"#\s*include\s*[<\"].*zpp", text), fn
+            assert "libzpp" not in text, fn

@@ -1,0 +1,170 @@
+"""GPU parity of zpp_dequant_reduce_requant against the CPU oracle.
+
+Codes and scales of the requantized sum must match bit for bit; the binary32
+sum must be within 1e-5 of the largest input scale of its block (and is
+expected bit-exact, both sides adding the same rounded terms in the same
+order). Covers 1..33 inputs (batches of four and remainders), 4- and 8-bit
+inputs and outputs, every block size, strided inputs with gaps, the
+hand-derived golden cases (order of summation, no fused multiply-add), and
+inputs quantized from workload-like data.
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import Guarded, assert_bits_equal, assert_within_scale, dev, need_gpu, torch
+
+pytestmark = pytest.mark.gpu
+
+BLOCKS = [32, 64, 128, 256, 512, 1024, 2048, 4096]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def _run(codes_np, cstride, scales_np, sstride, R, bits_in, numel, block, bits_out, want_sum=True):
+    """codes_np / scales_np hold R inputs at the given strides (bytes / floats)."""
+    import block_quantization_codec_amd as z
+    ci = dev(codes_np)
+    si = dev(scales_np)
+    gc = Guarded(numel * bits_out // 8) if bits_out else None
+    gs = Guarded(4 * (numel // block)) if bits_out else None
+    gu = Guarded(4 * numel) if want_sum else None
+    torch.cuda.synchronize()
+    z.zpp_dequant_reduce_requant(ci, cstride, si, sstride, R, bits_in, numel, block,
+                                 gc.ptr if gc else None, gs.ptr if gs else None, bits_out,
+                                 gu.ptr if gu else None)
+    torch.cuda.synchronize()
+    for g in (gc, gs, gu):
+        if g is not None:
+            assert g.untouched(), "write outside an output buffer"
+    return (gc.bytes() if gc else None, gs.as_np(np.float32) if gs else None,
+            gu.as_np(np.float32) if gu else None)
+
+
+def _inputs(R, bits_in, numel, block, seed, gap=0):
+    """R inputs quantized (by the oracle) from Student-t data of varying magnitude,
+    laid side by side with `gap` spare blocks between them."""
+    per_c = numel * bits_in // 8 + gap * block * bits_in // 8
+    per_s = numel // block + gap
+    codes = np.zeros(R * per_c, np.uint8)
+    scales = np.zeros(R * per_s, np.float32)
+    for r in range(R):
+        x = synth.bf16_student_t(numel, 3.0, 1e-4 * (1 + r % 3), (seed, r, numel, block))
+        c, s = oracle.quantize(x, block, bits_in)
+        codes[r * per_c:r * per_c + c.size] = c
+        scales[r * per_s:r * per_s + s.size] = s
+        if gap:
+            codes[r * per_c + c.size:(r + 1) * per_c] = 0xEE  # garbage the kernel must not read
+            scales[r * per_s + s.size:(r + 1) * per_s] = np.float32(7e30)
+    return codes, per_c, scales, per_s
+
+
+def _expect(codes, per_c, scales, per_s, R, bits_in, numel, block, bits_out):
+    cl = [codes[r * per_c:r * per_c + numel * bits_in // 8] for r in range(R)]
+    sl = [scales[r * per_s:r * per_s + numel // block] for r in range(R)]
+    co, so, su = oracle.dequant_reduce_requant(cl, sl, bits_in, numel, block, bits_out)
+    smax = np.max(np.stack(sl), axis=0)
+    return co, so, su, np.repeat(smax, block)
+
+
+def _check(R, bits_in, bits_out, block, numel, seed, gap=0, want_sum=True):
+    codes, pc, scales, ps = _inputs(R, bits_in, numel, block, seed, gap)
+    gco, gso, gsu = _run(codes, pc, scales, ps, R, bits_in, numel, block, bits_out, want_sum)
+    co, so, su, smax = _expect(codes, pc, scales, ps, R, bits_in, numel, block, bits_out)
+    what = f"R={R} in={bits_in} out={bits_out} B={block} n={numel}"
+    if want_sum:
+        assert_within_scale(gsu, su, smax, "sum " + what)
+        assert_bits_equal(gsu, su, "sum bits " + what)
+    if bits_out:
+        assert_bits_equal(gso, so, "scales " + what)
+        assert_bits_equal(gco, co, "codes " + what)
+
+
+@pytest.mark.parametrize("R", [1, 2, 3, 4, 5, 8, 9, 32, 33])
+@pytest.mark.parametrize("bits_in,bits_out", [(4, 4), (8, 8), (4, 0)])
+def test_input_counts(R, bits_in, bits_out):
+    _check(R, bits_in, bits_out, 256, 256 * 100, 1)
+
+
+@pytest.mark.parametrize("block", BLOCKS)
+@pytest.mark.parametrize("bits_in,bits_out", [(4, 4), (8, 8), (4, 8), (8, 4)])
+def test_block_sizes(block, bits_in, bits_out):
+    nb = max(2, 20_000 // block) + 1
+    _check(4, bits_in, bits_out, block, block * nb, 2)
+
+
+@pytest.mark.parametrize("bits_in,bits_out", [(4, 4), (8, 8)])
+def test_strided_inputs_with_gaps(bits_in, bits_out):
+    _check(5, bits_in, bits_out, 128, 128 * 333, 3, gap=7)
+
+
+def test_requant_only_without_sum():
+    _check(8, 4, 4, 256, 256 * 64, 4, want_sum=False)
+
+
+def test_random_code_bytes_and_scales():
+    """Arbitrary code patterns (including -8) and scales across binades."""
+    rng = np.random.default_rng(5)
+    R, block, numel = 6, 64, 64 * 300
+    codes = rng.integers(0, 256, R * numel // 2, dtype=np.uint8)
+    scales = np.exp2(rng.uniform(-30, 30, R * numel // block)).astype(np.float32)
+    gco, gso, gsu = _run(codes, numel // 2, scales, numel // block, R, 4, numel, block, 4)
+    cl = [codes[r * numel // 2:(r + 1) * numel // 2] for r in range(R)]
+    sl = [scales[r * numel // block:(r + 1) * numel // block] for r in range(R)]
+    co, so, su = oracle.dequant_reduce_requant(cl, sl, 4, numel, block, 4)
+    assert_bits_equal(gsu, su, "sum")
+    assert_bits_equal(gso, so, "scales")
+    assert_bits_equal(gco, co, "codes")
+
+
+def _pack(q, bits):
+    q = np.asarray(q, dtype=np.int64)
+    if bits == 8:
+        return (q & 0xFF).astype(np.uint8)
+    q = q & 0xF
+    return (q[0::2] | (q[1::2] << 4)).astype(np.uint8)
+
+
+def test_golden_reduce_cases_on_gpu():
+    """Hand-derived cases (blocks of 4) padded with zero codes to a block of 32."""
+    with open(os.path.join(os.path.dirname(__file__), "golden", "reduce_cases.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        bi, bo, R = c["bits_in"], c["bits_out"], len(c["inputs"])
+        codes = np.zeros(R * 32 * bi // 8, np.uint8)
+        scales = np.zeros(R, np.float32)
+        for r, inp in enumerate(c["inputs"]):
+            q = np.zeros(32, np.int64)
+            q[:4] = inp["codes"]
+            codes[r * 32 * bi // 8:(r + 1) * 32 * bi // 8] = _pack(q, bi)
+            if "scales_bits_hex" in inp:
+                scales[r] = np.array([int(inp["scales_bits_hex"][0], 16)], np.uint32).view(np.float32)[0]
+            else:
+                scales[r] = inp["scales"][0]
+        gco, gso, gsu = _run(codes, 32 * bi // 8, scales, 1, R, bi, 32, 32, bo)
+        assert gsu[:4].tolist() == c["sum"], c["name"]
+        assert not gsu[4:].any()
+        assert gso.tolist() == c["out_scales"], c["name"]
+        q = gco.view(np.int8).astype(np.int64) if bo == 8 else \
+            np.stack([(gco & 0xF).astype(np.int64), (gco >> 4).astype(np.int64)], 1).reshape(-1)
+        if bo == 4:
+            q = np.where(q >= 8, q - 16, q)
+        assert q[:4].tolist() == c["out_codes"], c["name"]
+
+
+def test_empty_is_a_no_op():
+    import block_quantization_codec_amd as z
+    # numel == 0 with a requested output is valid and launches nothing
+    g = Guarded(64)
+    z.zpp_dequant_reduce_requant(g.ptr, 0, g.ptr, 0, 4, 4, 0, 256, None, None, 0, g.ptr)
+    torch.cuda.synchronize()
+    assert g.all_canary()
