@@ -1,0 +1,375 @@
+"""Throughput of the ZeRO++ block-quantization codec on one MI355X.
+
+One step is one pass of the whole per-GPU hot path on resident HBM inputs:
+
+  qgZ, one GPU's share at 32 nodes x 8 GPUs (rank 255 = node 31, local 7),
+  500,000,000-element bf16 gradient bucket (Student-t nu=3 x 1e-4),
+  zero-padded to 256 slices of 1,953,280 elements, int4, block 256:
+    1. tensor-slice reorder of the bf16 bucket (256 slices)
+    2. one-shot int4 quantize of the reordered bucket (chunks 0-6 into the
+       send buffer, chunk 7 straight into its slot of the hop-1 receive buffer)
+    3. hop 1: 8-way dequantize + fp32 sum + int4 requantize of the receive
+       buffer (sub-chunks 0-30 into the hop-2 send buffer, sub-chunk 31 into
+       its slot of the hop-2 receive buffer)
+    4. hop 2: 32-way dequantize + fp32 sum into the owned fp32 shard
+  qwZ and qgZ on one 70B-scale GQA layer (hidden 8192, 64/8 heads, FFN 28672,
+  855,638,016 weights), N(0, 0.01) with 0.01 % outliers x100:
+    5. int8 block-512 quantize of the bf16 weight
+    6. dequantize of those codes back to bf16 (the gather side)
+    7. int4 block-128 quantize of the bf16 gradient
+
+The peers' hop-1 chunks and the other nodes' hop-2 pieces are drawn from the
+same distributions and quantized once before timing (the exchanges are not
+part of one GPU's work). Reported value: algorithmic input bytes of the seven
+kernels per step / step time (GB/s). Each kernel is also timed with HIP
+events on the stream it runs on, and the longest one is reported against the
+HBM roofline. The CPU baseline runs the plain C oracle (single thread) over
+the same seven kernels' work of one step, twice.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+
+# source files each kernel family is built from (for the traffic record's validity)
+KERNEL_SOURCES = {
+    "quantize": ["quantize.hip", "zpp_device.h"],
+    "dequantize": ["dequantize.hip", "zpp_device.h"],
+    "reorder": ["reorder.hip", "zpp_device.h"],
+    "drr": ["drr.hip", "zpp_device.h"],
+}
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash(family: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[family]:
+        with open(os.path.join(ROOT, "block_quantization_codec_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(kernel_key: str, family: str):
+    """Measured HBM bytes per launch from the committed rocprofv3 counter runs,
+    or None when absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != source_hash(family):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+class Step:
+    """Device buffers and the launch sequence of one step."""
+
+    def __init__(self, torch, z, log_fn=log):
+        import numpy as np
+
+        import synth
+
+        self.torch, self.z = torch, z
+        dev = torch.device("cuda")
+        c = synth.QGZ_INT4_32x8
+        self.c = c
+        n, g, B = c.n_nodes, c.gpus_per_node, c.block
+        P, S, C = c.padded, c.slice_len, c.chunk_len
+        self.node, self.local = n - 1, g - 1
+        rank = self.node * g + self.local
+
+        def to_dev(a):
+            t = torch.from_numpy(a)
+            if a.dtype == np.uint16:
+                t = t.view(torch.int16).view(torch.bfloat16)
+            return t.to(dev)
+
+        t0 = time.time()
+        log_fn(f"generating {c.name} rank {rank} ...")
+        self.bucket_np = c.bucket(rank)
+        self.bucket = to_dev(self.bucket_np)
+        self.reord = torch.empty_like(self.bucket)
+        # send / receive buffers (codes and scales) of the two hops
+        self.send1_c = torch.empty((g - 1) * C // 2, dtype=torch.uint8, device=dev)
+        self.send1_s = torch.empty((g - 1) * C // B, dtype=torch.float32, device=dev)
+        self.recv1_c = torch.empty(g * C // 2, dtype=torch.uint8, device=dev)
+        self.recv1_s = torch.empty(g * C // B, dtype=torch.float32, device=dev)
+        self.send2_c = torch.empty((n - 1) * S // 2, dtype=torch.uint8, device=dev)
+        self.send2_s = torch.empty((n - 1) * S // B, dtype=torch.float32, device=dev)
+        self.recv2_c = torch.empty(n * S // 2, dtype=torch.uint8, device=dev)
+        self.recv2_s = torch.empty(n * S // B, dtype=torch.float32, device=dev)
+        self.shard = torch.empty(S, dtype=torch.float32, device=dev)
+        # what the exchanges would deliver: peers' chunks and other nodes' pieces
+        for i in range(g - 1):
+            x = to_dev(c.peer_chunk(i, self.local, self.node))
+            z.zpp_quantize_blocks(x, z.ZPP_BF16, C, B, 4, self.recv1_c[i * C // 2:], self.recv1_s[i * C // B:])
+        for a in range(n - 1):
+            x = to_dev(c.node_partial(a, self.node, self.local))
+            z.zpp_quantize_blocks(x, z.ZPP_FP32, S, B, 4, self.recv2_c[a * S // 2:], self.recv2_s[a * S // B:])
+        torch.cuda.synchronize()
+        log_fn(f"generating GQA layer weight and gradient ... ({time.time() - t0:.1f}s so far)")
+        self.w_np = synth.gqa_weight()
+        self.g_np = synth.gqa_grad()
+        self.W = to_dev(self.w_np)
+        self.G = to_dev(self.g_np)
+        nw = self.W.numel()
+        self.wc = torch.empty(nw, dtype=torch.uint8, device=dev)
+        self.ws = torch.empty(nw // 512, dtype=torch.float32, device=dev)
+        self.wy = torch.empty_like(self.W)
+        self.gc = torch.empty(nw // 2, dtype=torch.uint8, device=dev)
+        self.gs = torch.empty(nw // 128, dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        log_fn(f"inputs resident in HBM ({time.time() - t0:.1f}s)")
+
+        # (name, kernel family, algorithmic input bytes, algorithmic output bytes, rocprof name fragment)
+        self.kernels = [
+            ("reorder_bf16_256slices", "reorder", 2 * P, 2 * P, "reorder_kernel<16>"),
+            ("quantize_int4_b256", "quantize", 2 * P, P // 2 + 4 * P // B, "quantize_kernel<4, 8, false> x2"),
+            ("hop1_drr_8way_int4_b256", "drr", g * (C // 2 + 4 * C // B), C // 2 + 4 * C // B,
+             "drr_kernel<4, 4, 8, 32> + drr_kernel<4, 4, 8, 8>"),
+            ("hop2_reduce_32way_fp32", "drr", n * (S // 2 + 4 * S // B), 4 * S, "drr_kernel<4, 0, 8, 8>"),
+            ("quantize_int8_b512_gqa_weight", "quantize", 2 * nw, nw + 4 * nw // 512,
+             "quantize_kernel<8, 9, false>"),
+            ("dequantize_int8_b512_gqa_weight", "dequantize", nw + 4 * nw // 512, 2 * nw,
+             "dequantize_kernel<8, false>"),
+            ("quantize_int4_b128_gqa_grad", "quantize", 2 * nw, nw // 2 + 4 * nw // 128,
+             "quantize_kernel<4, 7, false>"),
+        ]
+
+    def launches(self):
+        """One step: a list of zero-argument callables, one per kernel row."""
+        z, c = self.z, self.c
+        n, g, B = c.n_nodes, c.gpus_per_node, c.block
+        S, C = c.slice_len, c.chunk_len
+        loc, node = self.local, self.node
+        nw = self.W.numel()
+
+        def reorder():
+            z.zpp_reorder_slices(self.bucket, self.reord, 2 * S, n, g)
+
+        def quantize_grad():
+            z.zpp_quantize_blocks(self.reord, z.ZPP_BF16, loc * C, B, 4, self.send1_c, self.send1_s)
+            z.zpp_quantize_blocks(self.reord[loc * C:], z.ZPP_BF16, C, B, 4, self.recv1_c[loc * C // 2:],
+                                  self.recv1_s[loc * C // B:])
+
+        def hop1():
+            z.zpp_dequant_reduce_requant(self.recv1_c, C // 2, self.recv1_s, C // B, g, 4, node * S, B,
+                                         self.send2_c, self.send2_s, 4, None)
+            z.zpp_dequant_reduce_requant(self.recv1_c[node * S // 2:], C // 2, self.recv1_s[node * S // B:],
+                                         C // B, g, 4, S, B, self.recv2_c[node * S // 2:],
+                                         self.recv2_s[node * S // B:], 4, None)
+
+        def hop2():
+            z.zpp_dequant_reduce_requant(self.recv2_c, S // 2, self.recv2_s, S // B, n, 4, S, B, None, None, 0,
+                                         self.shard)
+
+        def qw():
+            z.zpp_quantize_blocks(self.W, z.ZPP_BF16, nw, 512, 8, self.wc, self.ws)
+
+        def dqw():
+            z.zpp_dequantize_blocks(self.wc, self.ws, 8, nw, 512, self.wy, z.ZPP_BF16)
+
+        def qg():
+            z.zpp_quantize_blocks(self.G, z.ZPP_BF16, nw, 128, 4, self.gc, self.gs)
+
+        return [reorder, quantize_grad, hop1, hop2, qw, dqw, qg]
+
+
+def cpu_baseline(step: "Step", frac: float = 1.0, passes: int = 2):
+    """The oracle, as it stands, on the first `frac` of every kernel's work,
+    `passes` times over (the host's single-thread oracle needs ~5-7 s a pass)."""
+    import numpy as np
+
+    import oracle
+
+    oracle.lib()
+    c = step.c
+    n, g, B = c.n_nodes, c.gpus_per_node, c.block
+    S = c.slice_len
+    sub_s = (int(S * frac) // B) * B           # a shorter slice, same slicing
+    nw = step.w_np.size
+    w_n = (int(nw * frac) // 512) * 512
+    g_n = (int(nw * frac) // 128) * 128
+    bucket = step.bucket_np.reshape(n * g, S)[:, :sub_s].reshape(-1)
+    hop_n = (int(c.chunk_len * frac) // B) * B
+    hop2_n = sub_s
+    hc, hs = oracle.quantize(bucket[:hop_n], B, 4)      # hop inputs (their values do not change the work)
+    hop_inputs_c = [hc] * g
+    hop_inputs_s = [hs] * g
+    h2c, h2s = oracle.quantize(bucket[:hop2_n], B, 4)
+    timings = []
+
+    def timed(name, in_bytes, fn):
+        t = time.perf_counter()
+        out = fn()
+        timings.append((name, in_bytes, time.perf_counter() - t))
+        return out
+
+    for _ in range(passes):
+        re_ = timed("reorder", bucket.nbytes, lambda: oracle.reorder_slices(bucket, n, g))
+        timed("quantize_int4_b256", re_.nbytes, lambda: oracle.quantize(re_, B, 4))
+        timed("hop1", g * (hop_n // 2 + 4 * hop_n // B),
+              lambda: oracle.dequant_reduce_requant(hop_inputs_c, hop_inputs_s, 4, hop_n, B, 4))
+        timed("hop2", n * (hop2_n // 2 + 4 * hop2_n // B),
+              lambda: oracle.dequant_reduce_requant([h2c] * n, [h2s] * n, 4, hop2_n, B, 0))
+        wq = timed("quantize_int8_b512", 2 * w_n, lambda: oracle.quantize(step.w_np[:w_n], 512, 8))
+        timed("dequantize_int8_b512", w_n + 4 * w_n // 512,
+              lambda: oracle.dequantize(wq[0], wq[1], 8, w_n, 512, out="bf16"))
+        timed("quantize_int4_b128", 2 * g_n, lambda: oracle.quantize(step.g_np[:g_n], 128, 4))
+    total_in = sum(t[1] for t in timings)
+    total_s = sum(t[2] for t in timings)
+    return {
+        "value": round(total_in / total_s / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{'all' if frac == 1.0 else f'first {frac:g}'} of every kernel's work in one step "
+                   f"({sub_s}-element slices, {hop_n}-element hop-1 chunk, {w_n}/{g_n} GQA elements), "
+                   f"{passes} passes: {total_in / 1e9:.2f} GB of input in {total_s:.1f} s, single-threaded C"),
+        "seconds": round(total_s, 2),
+        "per_kernel_s": {name: round(sum(t[2] for t in timings if t[0] == name), 3)
+                         for name in dict.fromkeys(t[0] for t in timings)},
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU's share of the codec and runs on exactly one GPU; "
+              f"--gpus {args.gpus} (WORLD_SIZE {world}) is not supported: collectives are out of scope "
+              "and every rank's work is the same per-GPU kernel sequence.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import block_quantization_codec_amd as z
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+
+    # plain copy of known size, for scaling the rocprofv3 byte counters
+    cal_src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    cal_dst = torch.empty_like(cal_src)
+    cal_dst.copy_(cal_src)
+    torch.cuda.synchronize()
+    del cal_src, cal_dst
+
+    step = Step(torch, z)
+    fns = step.launches()
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fns]
+          for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        for i, f in enumerate(fns):
+            ev[k][i][0].record(stream)
+            f()
+            ev[k][i][1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / K
+
+    per = []
+    for i, (name, fam, rin, wout, kname) in enumerate(step.kernels):
+        ms = sum(ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(K)) / K
+        per.append((name, fam, rin, wout, kname, ms))
+    total_in = sum(p[2] for p in per)
+    total_rw = sum(p[2] + p[3] for p in per)
+    value = total_in / (ms_per_step * 1e-3) / 1e9
+
+    dom = max(per, key=lambda p: p[5])
+    name, fam, rin, wout, kname, ms = dom
+    achieved = (rin + wout) / (ms * 1e-3) / 1e9
+    traffic = traffic_record(name, fam)
+    roofline = {
+        "bound": "hbm",
+        "kernel": name,
+        "rocprof_name": kname,
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBPS, 4),
+        "traffic": traffic,
+        "algorithmic_bytes": rin + wout,
+        "avg_launch_ms": round(ms, 5),
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(step)
+
+    line = {
+        "metric": "quantize / dequant-reduce-requant input GB/s and % of HBM peak, 1 MI355X",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": ("qgZ 32x8 rank-255 share of a 500M-element bf16 gradient bucket (reorder, int4 "
+                         "B=256 quantize, 8-way hop-1 dequant-reduce-requant, 32-way hop-2 fp32 reduce) + "
+                         "qwZ/qgZ on one 855,638,016-parameter GQA layer (int8 B=512 quantize and "
+                         "dequantize of the weight, int4 B=128 quantize of the gradient)"),
+            "bucket_elems": c_bucket(step),
+            "gqa_layer_elems": step.W.numel(),
+            "topology": "32 nodes x 8 GPUs (simulated; one GPU's share)",
+            "parallelism": "none (one GPU's share of ZeRO++ data parallelism)",
+        },
+        "hbm_frac_step": round(total_rw / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "kernels": {p[0]: {"ms": round(p[5], 5), "in_GBps": round(p[2] / (p[5] * 1e-3) / 1e9, 1),
+                           "rw_GBps": round((p[2] + p[3]) / (p[5] * 1e-3) / 1e9, 1),
+                           "hbm_frac": round((p[2] + p[3]) / (p[5] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+                    for p in per},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def c_bucket(step) -> int:
+    return step.c.numel
+
+
+if __name__ == "__main__":
+    sys.exit(main())

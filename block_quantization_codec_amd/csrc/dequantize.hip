@@ -18,7 +18,10 @@ namespace {
 
 constexpr int kE = 8;              // elements per lane per segment
 constexpr int kSeg = kWave * kE;   // 512
-constexpr int kU = 4;              // segments per tile
+#ifndef ZPP_DEQUANT_SEGS
+#define ZPP_DEQUANT_SEGS 1
+#endif
+constexpr int kU = ZPP_DEQUANT_SEGS;  // segments per tile
 constexpr int kTile = kU * kSeg;
 
 template <int BITS, bool F32OUT>
@@ -39,11 +42,11 @@ __global__ __launch_bounds__(kBlockThreads) void dequantize_kernel(const uint8_t
             ok[u] = e0 < numel;
             const int64_t e = ok[u] ? e0 : 0;
             if constexpr (BITS == 8) {
-                const u32x2 c = ld<u32x2>(codes + e);
+                const u32x2 c = ld_stream<u32x2>(codes + e);
                 w[u][0] = c[0];
                 w[u][1] = c[1];
             } else {
-                w[u][0] = ld<uint32_t>(codes + e / 2);
+                w[u][0] = ld_stream<uint32_t>(codes + e / 2);
                 w[u][1] = 0;
             }
             s[u] = scales[e >> log2b];

@@ -9,51 +9,138 @@
 // Partitioning": GPU i keeps shard i, whose optimizer step works in fp32).
 //
 // Arithmetic contract: for each element, acc = +0; for r = 0..R-1 in order,
-// acc = fl(acc + fl(code_r * s_r)). The first term is formed as
-// fma(code_0, s_0, +0), which equals fl(+0 + fl(code_0 * s_0)) exactly (one
-// rounding of the exact product; a nonzero integer code times a nonzero
-// scale never rounds to zero); every later product and sum is rounded on its
-// own, never fused.
+// acc = fl(acc + fl(code_r * s_r)), every product and every sum rounded on
+// its own, never fused. Scales are non-negative (they are block maxima over
+// Q), so no product is -0 and +0 + the first product is that product.
 //
-// Layout of the work: a lane owns 32 consecutive elements of a 2048-element
-// wave segment, i.e. one 16-byte vector of 4-bit codes (two of 8-bit codes)
-// per input, so each load instruction reads one contiguous kilobyte of an
-// input. Inputs are read four at a time, all loads of a batch in flight
-// before the batch is summed in input order. The requantized block maximum
-// is reduced across the block's lanes with DPP / permlane swaps.
+// Layout of the work: a lane owns E consecutive elements of a wave segment of
+// 64 E elements: E = 32 (one 16-byte vector of 4-bit codes per input, so
+// each load instruction reads one contiguous kilobyte of an input), or E = 8
+// for small outputs, which then still spread over every SIMD. Inputs are
+// read a batch at a time, all loads of a batch in flight before the batch is
+// summed in input order. The requantized block maximum is reduced across the
+// block's lanes with DPP / permlane swaps.
 #include "zpp_device.h"
 #include "zpp_launch.h"
 
 namespace zpp {
 namespace {
 
-constexpr int kE = 32;              // elements per lane per segment
-constexpr int kSeg = kWave * kE;    // 2048
-constexpr int kRB = 4;              // inputs per load batch
+#ifndef ZPP_DRR_BATCH
+#define ZPP_DRR_BATCH 8
+#endif
+constexpr int kRB = ZPP_DRR_BATCH;  // inputs per load batch
+// Below this many waves at 32 elements per lane, lanes take 8 elements each
+// so that small outputs still spread over every SIMD.
+#ifndef ZPP_DRR_NARROW_WAVES
+#define ZPP_DRR_NARROW_WAVES 8192
+#endif
 
-template <int BITS_IN_, int BITS_OUT, int LOG2B_>
+template <int BITS_IN_, int BITS_OUT, int LOG2B_, int E_>
 struct DrrGeom {
     static constexpr int BITS_IN = BITS_IN_;
     static constexpr int LOG2B = LOG2B_;
+    static constexpr int E = E_;                           // elements per lane per segment
+    static constexpr int SEG = kWave * E;                  // elements per wave segment
     static constexpr int B = 1 << LOG2B;
-    static constexpr int SPB = B > kSeg ? B / kSeg : 1;    // segments per block (= per tile)
-    static constexpr int L = B >= kSeg ? kWave : B / kE;   // lanes per block within a segment
+    static constexpr int SPB = B > SEG ? B / SEG : 1;      // segments per block (= per tile)
+    static constexpr int L = B >= SEG ? kWave : B / E;     // lanes per block within a segment
     static constexpr int U = SPB;
-    static constexpr int TILE = U * kSeg;
-    static constexpr int NV = kE * BITS_IN / 8 / 16;       // 16-byte vectors per lane per input
+    static constexpr int TILE = U * SEG;
+    static constexpr int ND = E * BITS_IN / 32;            // code dwords per lane per input
     static constexpr int QMAX = BITS_OUT == 8 ? 127 : 7;
 };
 
+template <int ND>
+__device__ __forceinline__ void load_dwords(const uint8_t *p, uint32_t (&d)[ND]) {
+    if constexpr (ND == 1) {
+        d[0] = ld_stream<uint32_t>(p);
+    } else if constexpr (ND == 2) {
+        const u32x2 v = ld_stream<u32x2>(p);
+        d[0] = v[0];
+        d[1] = v[1];
+    } else {
+#pragma unroll
+        for (int j = 0; j < ND / 4; ++j) {
+            const u32x4 v = ld_stream<u32x4>(p + 16 * j);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) d[4 * j + i] = v[i];
+        }
+    }
+}
+
+template <int ND>
+__device__ __forceinline__ void store_dwords(uint8_t *p, const uint32_t (&d)[ND]) {
+    if constexpr (ND == 1) {
+        st<uint32_t>(p, d[0]);
+    } else if constexpr (ND == 2) {
+        st<u32x2>(p, u32x2{d[0], d[1]});
+    } else {
+#pragma unroll
+        for (int j = 0; j < ND / 4; ++j) st<u32x4>(p + 16 * j, u32x4{d[4 * j], d[4 * j + 1], d[4 * j + 2], d[4 * j + 3]});
+    }
+}
+
+// The codes of dword `w` of one input as binary32 products code * s, element
+// 0 first. FAST (4-bit codes only): a nibble moved to the top of a byte reads
+// as the signed byte 16 * code, and (16 * code) * (s / 16) is the same real
+// product as code * s, so it rounds identically whenever s / 16 is exact
+// (s == 0 or s >= 2^-122). 8-bit codes convert directly.
+template <int BITS_IN, bool FAST>
+__device__ __forceinline__ void dequant_dword(uint32_t w, float s, float s16, float (&p)[32 / BITS_IN]) {
+    if constexpr (BITS_IN == 8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = static_cast<float>(static_cast<int8_t>(w >> (8 * i))) * s;
+    } else if constexpr (FAST) {
+        const uint32_t even = (w << 4) & 0xF0F0F0F0u;  // byte i: code 2i << 4
+        const uint32_t odd = w & 0xF0F0F0F0u;          // byte i: code 2i+1 << 4
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p[2 * i] = static_cast<float>(static_cast<int8_t>(even >> (8 * i))) * s16;
+            p[2 * i + 1] = static_cast<float>(static_cast<int8_t>(odd >> (8 * i))) * s16;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p[i] = static_cast<float>(code_at<4>(w, i)) * s;
+    }
+}
+
+// Sum one batch of loaded inputs into acc, in input order.
+template <typename G, int NB, bool FIRST, bool FAST>
+__device__ __forceinline__ void accumulate(const uint32_t (&w)[NB][G::U][G::ND], const float (&s)[NB][G::U],
+                                           float (&acc)[G::U][G::E]) {
+    constexpr int CPW = 32 / G::BITS_IN;  // codes per dword
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+#pragma unroll
+        for (int u = 0; u < G::U; ++u) {
+            const float sk = s[k][u];
+            const float s16 = sk * 0.0625f;
+#pragma unroll
+            for (int d = 0; d < G::ND; ++d) {
+                float p[CPW];
+                dequant_dword<G::BITS_IN, FAST>(w[k][u][d], sk, s16, p);
+#pragma unroll
+                for (int i = 0; i < CPW; ++i) {
+                    if (FIRST && k == 0)
+                        acc[u][d * CPW + i] = p[i];
+                    else
+                        acc[u][d * CPW + i] = acc[u][d * CPW + i] + p[i];
+                }
+            }
+        }
+    }
+}
+
 // Add inputs r0 .. r0+NB-1 (in that order) into acc. FIRST: input r0 starts
-// the sums (acc = fma(q, s, +0), equal to +0 + fl(q * s)).
+// the sums: acc = +0 + p, where p is never -0 (a zero code gives +0 for a
+// non-negative scale), so acc = p.
 template <typename G, int NB, bool FIRST>
 __device__ __forceinline__ void sum_batch(const uint8_t *__restrict__ codes_in, int64_t codes_stride,
                                           const float *__restrict__ scales_in, int64_t scales_stride, int r0,
-                                          const int64_t (&e)[G::U], float (&acc)[G::U][kE]) {
-    constexpr int U = G::U, NV = G::NV, BITS_IN = G::BITS_IN;
-    constexpr int WPV = 4;                 // dwords per vector
-    constexpr int CPW = 32 / BITS_IN;      // codes per dword
-    u32x4 w[NB][U][NV];
+                                          const int64_t (&e)[G::U], float (&acc)[G::U][G::E]) {
+    constexpr int U = G::U, BITS_IN = G::BITS_IN;
+    uint32_t w[NB][U][G::ND];
     float s[NB][U];
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
@@ -61,29 +148,26 @@ __device__ __forceinline__ void sum_batch(const uint8_t *__restrict__ codes_in, 
         const float *sc = scales_in + static_cast<int64_t>(r0 + k) * scales_stride;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-#pragma unroll
-            for (int v = 0; v < NV; ++v) w[k][u][v] = ld<u32x4>(c + e[u] * BITS_IN / 8 + 16 * v);
+            load_dwords<G::ND>(c + e[u] * BITS_IN / 8, w[k][u]);
             s[k][u] = sc[e[u] >> G::LOG2B];
         }
     }
+    if constexpr (BITS_IN == 8) {
+        accumulate<G, NB, FIRST, true>(w, s, acc);
+    } else {
+        bool fast = true;
 #pragma unroll
-    for (int k = 0; k < NB; ++k) {
+        for (int k = 0; k < NB; ++k)
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-#pragma unroll
-            for (int i = 0; i < kE; ++i) {
-                const uint32_t word = w[k][u][i / (CPW * WPV)][(i / CPW) % WPV];
-                const float q = static_cast<float>(code_at<BITS_IN>(word, i % CPW));
-                if (FIRST && k == 0)
-                    acc[u][i] = __builtin_fmaf(q, s[k][u], 0.0f);
-                else
-                    acc[u][i] = acc[u][i] + q * s[k][u];
-            }
-        }
+            for (int u = 0; u < U; ++u) fast &= (s[k][u] == 0.0f) | (s[k][u] >= 0x1p-122f);
+        if (fast)
+            accumulate<G, NB, FIRST, true>(w, s, acc);
+        else
+            accumulate<G, NB, FIRST, false>(w, s, acc);
     }
 }
 
-template <int BITS_IN, int BITS_OUT, int LOG2B>
+template <int BITS_IN, int BITS_OUT, int LOG2B, int E>
 __global__ __launch_bounds__(kBlockThreads) void drr_kernel(const uint8_t *__restrict__ codes_in,
                                                             int64_t codes_stride,
                                                             const float *__restrict__ scales_in,
@@ -91,7 +175,7 @@ __global__ __launch_bounds__(kBlockThreads) void drr_kernel(const uint8_t *__res
                                                             uint8_t *__restrict__ codes_out,
                                                             float *__restrict__ scales_out,
                                                             float *__restrict__ sum_out) {
-    using G = DrrGeom<BITS_IN, BITS_OUT, LOG2B>;
+    using G = DrrGeom<BITS_IN, BITS_OUT, LOG2B, E>;
     constexpr int U = G::U;
 
     const int lane = threadIdx.x & (kWave - 1);
@@ -103,12 +187,12 @@ __global__ __launch_bounds__(kBlockThreads) void drr_kernel(const uint8_t *__res
         bool ok[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t e0 = t0 + static_cast<int64_t>(u) * kSeg + lane * kE;
+            const int64_t e0 = t0 + static_cast<int64_t>(u) * G::SEG + lane * E;
             ok[u] = e0 < numel;
             e[u] = ok[u] ? e0 : 0;
         }
 
-        float acc[U][kE];
+        float acc[U][E];
         // Inputs are consumed in batches whose loads are all issued before
         // the batch is summed; the first batch starts the sums.
         int r = 0;
@@ -129,7 +213,7 @@ __global__ __launch_bounds__(kBlockThreads) void drr_kernel(const uint8_t *__res
                 if (!ok[u]) continue;
                 float *dst = sum_out + e[u];
 #pragma unroll
-                for (int v = 0; v < kE / 4; ++v)
+                for (int v = 0; v < E / 4; ++v)
                     st<u32x4>(dst + 4 * v, u32x4{as_u(acc[u][4 * v]), as_u(acc[u][4 * v + 1]),
                                                  as_u(acc[u][4 * v + 2]), as_u(acc[u][4 * v + 3])});
             }
@@ -140,42 +224,45 @@ __global__ __launch_bounds__(kBlockThreads) void drr_kernel(const uint8_t *__res
 #pragma unroll
             for (int u = 0; u < U; ++u)
 #pragma unroll
-                for (int i = 0; i < kE; ++i) mx = max(mx, as_u(acc[u][i]) & 0x7FFFFFFFu);
+                for (int i = 0; i < E; ++i) mx = max(mx, as_u(acc[u][i]) & 0x7FFFFFFFu);
             if (!ok[0]) mx = 0;
             mx = group_max_u32<G::L>(mx);
-            const float sc = as_f(mx) / static_cast<float>(G::QMAX);  // correctly rounded division
+            const float sc = block_scale<G::QMAX>(as_f(mx));
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                int32_t q[kE];
-                quantize_values<kE, G::QMAX>(acc[u], sc, q);
+                float mg[E];
+                round_codes<E, BITS_OUT>(acc[u], sc, mg);
+                uint32_t cw[E * BITS_OUT / 32];
+                pack_codes<E, BITS_OUT>(mg, cw);
                 if (!ok[u]) continue;
-                uint8_t *dst = codes_out + e[u] * BITS_OUT / 8;
-                if constexpr (BITS_OUT == 4) {
-                    st<u32x4>(dst, u32x4{pack_i4x8(q), pack_i4x8(q + 8), pack_i4x8(q + 16), pack_i4x8(q + 24)});
-                } else {
-#pragma unroll
-                    for (int v = 0; v < 2; ++v)
-                        st<u32x4>(dst + 16 * v,
-                                  u32x4{pack_i8x4(q[16 * v], q[16 * v + 1], q[16 * v + 2], q[16 * v + 3]),
-                                        pack_i8x4(q[16 * v + 4], q[16 * v + 5], q[16 * v + 6], q[16 * v + 7]),
-                                        pack_i8x4(q[16 * v + 8], q[16 * v + 9], q[16 * v + 10], q[16 * v + 11]),
-                                        pack_i8x4(q[16 * v + 12], q[16 * v + 13], q[16 * v + 14], q[16 * v + 15])});
-                }
+                store_dwords<E * BITS_OUT / 32>(codes_out + e[u] * BITS_OUT / 8, cw);
                 if (u == 0 && (lane & (G::L - 1)) == 0) scales_out[e[u] >> LOG2B] = sc;
             }
         }
     }
 }
 
-template <int BITS_IN, int BITS_OUT, int LOG2B>
-hipError_t launch(const void *codes_in, int64_t cstride, const float *scales_in, int64_t sstride, int n_inputs,
-                  int64_t numel, void *codes_out, float *scales_out, float *sum_out, hipStream_t stream) {
-    using G = DrrGeom<BITS_IN, BITS_OUT, LOG2B>;
+template <int BITS_IN, int BITS_OUT, int LOG2B, int E>
+hipError_t launch_e(const void *codes_in, int64_t cstride, const float *scales_in, int64_t sstride, int n_inputs,
+                    int64_t numel, void *codes_out, float *scales_out, float *sum_out, hipStream_t stream) {
+    using G = DrrGeom<BITS_IN, BITS_OUT, LOG2B, E>;
     const int64_t tiles = (numel + G::TILE - 1) / G::TILE;
-    drr_kernel<BITS_IN, BITS_OUT, LOG2B><<<stream_grid(tiles), kBlockThreads, 0, stream>>>(
+    drr_kernel<BITS_IN, BITS_OUT, LOG2B, E><<<stream_grid(tiles), kBlockThreads, 0, stream>>>(
         static_cast<const uint8_t *>(codes_in), cstride, scales_in, sstride, n_inputs, numel,
         static_cast<uint8_t *>(codes_out), scales_out, sum_out);
     return hipGetLastError();
+}
+
+template <int BITS_IN, int BITS_OUT, int LOG2B>
+hipError_t launch(const void *codes_in, int64_t cstride, const float *scales_in, int64_t sstride, int n_inputs,
+                  int64_t numel, void *codes_out, float *scales_out, float *sum_out, hipStream_t stream) {
+    using Wide = DrrGeom<BITS_IN, BITS_OUT, LOG2B, 32>;
+    const int64_t wide_waves = (numel + Wide::TILE - 1) / Wide::TILE;
+    if (wide_waves >= ZPP_DRR_NARROW_WAVES)
+        return launch_e<BITS_IN, BITS_OUT, LOG2B, 32>(codes_in, cstride, scales_in, sstride, n_inputs, numel,
+                                                      codes_out, scales_out, sum_out, stream);
+    return launch_e<BITS_IN, BITS_OUT, LOG2B, 8>(codes_in, cstride, scales_in, sstride, n_inputs, numel, codes_out,
+                                                 scales_out, sum_out, stream);
 }
 
 template <int BITS_IN, int BITS_OUT>

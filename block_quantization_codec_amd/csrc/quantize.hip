@@ -19,6 +19,11 @@
 #include "zpp_device.h"
 #include "zpp_launch.h"
 
+// Segments (16-byte loads per lane) per wave tile.
+#ifndef ZPP_QUANT_SEGS
+#define ZPP_QUANT_SEGS 2
+#endif
+
 namespace zpp {
 namespace {
 
@@ -30,7 +35,7 @@ struct QuantGeom {
     static constexpr int SEG = kWave * E;               // elements per wave segment
     static constexpr int SPB = B > SEG ? B / SEG : 1;   // segments per block
     static constexpr int L = B >= SEG ? kWave : B / E;  // lanes per block within a segment
-    static constexpr int U = SPB > 4 ? SPB : 4;         // segments per tile
+    static constexpr int U = SPB > ZPP_QUANT_SEGS ? SPB : ZPP_QUANT_SEGS;  // segments per tile
     static constexpr int NB = U / SPB;                  // scale slots per lane per tile
     static constexpr int TILE = U * SEG;
     static constexpr int CB = E * BITS / 8;             // code bytes per lane per segment
@@ -43,42 +48,47 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_kernel(const uint8_t *
                                                                  float *__restrict__ scales) {
     using G = QuantGeom<BITS, LOG2B, F32IN>;
     constexpr int E = G::E, U = G::U, SPB = G::SPB, NB = G::NB;
+    constexpr int CW = E * BITS / 32;  // code dwords per lane per segment (E * BITS / 32 >= 1)
 
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t wave = static_cast<int64_t>(blockIdx.x) * (kBlockThreads / kWave) + (threadIdx.x / kWave);
     const int64_t n_waves = static_cast<int64_t>(gridDim.x) * (kBlockThreads / kWave);
 
     for (int64_t t0 = wave * G::TILE; t0 < numel; t0 += n_waves * G::TILE) {
-        float v[U][E];
-        bool ok[U];
         // Issue every load of the tile first. Out-of-range lanes (only in the
         // last tile, and only for whole blocks since numel % B == 0) read
         // element 0 instead and are masked out afterwards.
         u32x4 raw[U];
+        bool ok[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t e0 = t0 + static_cast<int64_t>(u) * G::SEG + lane * E;
             ok[u] = e0 < numel;
-            raw[u] = ld<u32x4>(x + (ok[u] ? e0 : 0) * G::IB);
+            raw[u] = ld_stream<u32x4>(x + (ok[u] ? e0 : 0) * G::IB);
         }
+        float v[U][E];
         uint32_t m[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if constexpr (F32IN) {
+            uint32_t w[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) v[u][i] = ok[u] ? as_f(raw[u][i]) : 0.0f;
+            for (int i = 0; i < 4; ++i) w[i] = ok[u] ? raw[u][i] : 0u;
+            if constexpr (F32IN) {
+                uint32_t mx = 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    v[u][i] = as_f(w[i]);
+                    mx = max(mx, w[i] & 0x7FFFFFFFu);
+                }
+                m[u] = mx;
             } else {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const uint32_t w = ok[u] ? raw[u][i] : 0u;
-                    v[u][2 * i] = bf16_lo(w);
-                    v[u][2 * i + 1] = bf16_hi(w);
+                    v[u][2 * i] = bf16_lo(w[i]);
+                    v[u][2 * i + 1] = bf16_hi(w[i]);
                 }
+                m[u] = bf16_absmax_bits<4>(w);
             }
-            uint32_t mx = 0;
-#pragma unroll
-            for (int i = 0; i < E; ++i) mx = max(mx, as_u(v[u][i]) & 0x7FFFFFFFu);
-            m[u] = mx;
         }
 
         // Block absmax -> scale, one per block (per segment when SPB == 1).
@@ -89,30 +99,27 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_kernel(const uint8_t *
 #pragma unroll
             for (int k = 0; k < SPB; ++k) mx = max(mx, m[b * SPB + k]);
             mx = group_max_u32<G::L>(mx);
-            s[b] = as_f(mx) / static_cast<float>(G::QMAX);  // correctly rounded division
+            s[b] = block_scale<G::QMAX>(as_f(mx));
         }
 
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t e0 = t0 + static_cast<int64_t>(u) * G::SEG + lane * E;
-            int32_t q[E];
-            quantize_values<E, G::QMAX>(v[u], s[u / SPB], q);
+            float mg[E];
+            round_codes<E, BITS>(v[u], s[u / SPB], mg);
+            uint32_t cw[CW > 0 ? CW : 1];
+            if constexpr (CW > 0) pack_codes<E, BITS>(mg, cw);
             if (!ok[u]) continue;
             uint8_t *dst = codes + e0 * BITS / 8;
-            if constexpr (BITS == 8) {
-                if constexpr (E == 8)
-                    st<u32x2>(dst, u32x2{pack_i8x4(q[0], q[1], q[2], q[3]), pack_i8x4(q[4], q[5], q[6], q[7])});
-                else
-                    st<uint32_t>(dst, pack_i8x4(q[0], q[1], q[2], q[3]));
-            } else {
-                if constexpr (E == 8) {
-                    st<uint32_t>(dst, pack_i4x8(q));
-                } else {
-                    const uint32_t w = (static_cast<uint32_t>(q[0]) & 0xF) | ((static_cast<uint32_t>(q[1]) & 0xF) << 4) |
-                                       ((static_cast<uint32_t>(q[2]) & 0xF) << 8) |
-                                       ((static_cast<uint32_t>(q[3]) & 0xF) << 12);
-                    st<uint16_t>(dst, static_cast<uint16_t>(w));
-                }
+            if constexpr (CW == 2) {
+                st<u32x2>(dst, u32x2{cw[0], cw[1]});
+            } else if constexpr (CW == 1) {
+                st<uint32_t>(dst, cw[0]);
+            } else {  // fp32 input, 4-bit codes: 4 nibbles (offset binary) per lane
+                const uint32_t p0 = (as_u(mg[1]) << 4) | (as_u(mg[0]) & 0xFu);
+                const uint32_t p1 = (as_u(mg[3]) << 4) | (as_u(mg[2]) & 0xFu);
+                const uint32_t half = __builtin_amdgcn_perm(p1, p0, 0x0C0C0400u) ^ 0x8888u;
+                st<uint16_t>(dst, static_cast<uint16_t>(half));
             }
             if constexpr (SPB == 1) {
                 if ((lane & (G::L - 1)) == 0) scales[e0 >> LOG2B] = s[u];

@@ -49,7 +49,7 @@ __global__ __launch_bounds__(kBlockThreads) void reorder_kernel(const uint8_t *_
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             const int64_t i = t0 + u * kBlockThreads + threadIdx.x;
-            v[u] = ld<T>(s + (i < n_vec ? i : 0) * V);
+            v[u] = ld_stream<T>(s + (i < n_vec ? i : 0) * V);
         }
 #pragma unroll
         for (int u = 0; u < kU; ++u) {

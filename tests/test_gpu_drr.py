@@ -168,3 +168,23 @@ def test_empty_is_a_no_op():
     z.zpp_dequant_reduce_requant(g.ptr, 0, g.ptr, 0, 4, 4, 0, 256, None, None, 0, g.ptr)
     torch.cuda.synchronize()
     assert g.all_canary()
+
+
+@pytest.mark.parametrize("bits_in,bits_out,R", [(4, 4, 8), (8, 8, 3), (4, 0, 5)])
+def test_wide_lane_path(bits_in, bits_out, R):
+    """Outputs large enough for the 32-elements-per-lane layout (at least 8192 waves of
+    2048 elements), with a ragged tail; the small cases above use 8 elements per lane."""
+    block = 256
+    numel = 8192 * 2048 + 3 * 2048 + 5 * block
+    rng = np.random.default_rng([R, bits_in])
+    per_c = numel * bits_in // 8
+    codes = rng.integers(0, 256, R * per_c, dtype=np.uint8)
+    scales = np.exp2(rng.uniform(-20, -5, R * (numel // block))).astype(np.float32)
+    gco, gso, gsu = _run(codes, per_c, scales, numel // block, R, bits_in, numel, block, bits_out)
+    cl = [codes[r * per_c:(r + 1) * per_c] for r in range(R)]
+    sl = [scales[r * (numel // block):(r + 1) * (numel // block)] for r in range(R)]
+    co, so, su = oracle.dequant_reduce_requant(cl, sl, bits_in, numel, block, bits_out)
+    assert_bits_equal(gsu, su, "sum (wide lanes)")
+    if bits_out:
+        assert_bits_equal(gso, so, "scales (wide lanes)")
+        assert_bits_equal(gco, co, "codes (wide lanes)")
