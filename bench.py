@@ -5,9 +5,10 @@ One step is one pass of the whole per-GPU hot path on resident HBM inputs:
   qgZ, one GPU's share at 32 nodes x 8 GPUs (rank 255 = node 31, local 7),
   500,000,000-element bf16 gradient bucket (Student-t nu=3 x 1e-4),
   zero-padded to 256 slices of 1,953,280 elements, int4, block 256:
-    1. tensor-slice reorder of the bf16 bucket (256 slices)
-    2. one-shot int4 quantize of the reordered bucket (chunks 0-6 into the
-       send buffer, chunk 7 straight into its slot of the hop-1 receive buffer)
+    1+2. tensor-slice reorder fused into the one-shot int4 quantize: the
+       kernel reads the bucket in reordered slice order (chunks 0-6 of the
+       reordered bucket into the send buffer, chunk 7 straight into its slot
+       of the hop-1 receive buffer); the reordered bf16 bucket is never written
     3. hop 1: 8-way dequantize + fp32 sum + int4 requantize of the receive
        buffer (sub-chunks 0-30 into the hop-2 send buffer, sub-chunk 31 into
        its slot of the hop-2 receive buffer)
@@ -20,11 +21,14 @@ One step is one pass of the whole per-GPU hot path on resident HBM inputs:
 
 The peers' hop-1 chunks and the other nodes' hop-2 pieces are drawn from the
 same distributions and quantized once before timing (the exchanges are not
-part of one GPU's work). Reported value: algorithmic input bytes of the seven
-kernels per step / step time (GB/s). Each kernel is also timed with HIP
+part of one GPU's work). Reported value: algorithmic input bytes of the six
+kernel rows per step / step time (GB/s). The unfused pair (standalone reorder,
+then quantize of the reordered buffer) is timed after the steps and reported
+beside them. Each kernel is also timed with HIP
 events on the stream it runs on, and the longest one is reported against the
 HBM roofline. The CPU baseline runs the plain C oracle (single thread) over
-the same seven kernels' work of one step, twice.
+the same work as one step (the reorder and the quantize as two oracle steps),
+twice.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -139,9 +143,14 @@ class Step:
         log_fn(f"inputs resident in HBM ({time.time() - t0:.1f}s)")
 
         # (name, kernel family, algorithmic input bytes, algorithmic output bytes, rocprof name fragment)
-        self.kernels = [
+        self.unfused_kernels = [
             ("reorder_bf16_256slices", "reorder", 2 * P, 2 * P, "reorder_kernel<16>"),
-            ("quantize_int4_b256", "quantize", 2 * P, P // 2 + 4 * P // B, "quantize_kernel<4, 8, false> x2"),
+            ("quantize_int4_b256_of_reordered", "quantize", 2 * P, P // 2 + 4 * P // B,
+             "quantize_kernel<4, 8, false> x2"),
+        ]
+        self.kernels = [
+            ("reorder_quantize_int4_b256", "quantize", 2 * P, P // 2 + 4 * P // B,
+             "quantize_kernel<4, 8, false> x2"),
             ("hop1_drr_8way_int4_b256", "drr", g * (C // 2 + 4 * C // B), C // 2 + 4 * C // B,
              "drr_kernel<4, 4, 8, 32> + drr_kernel<4, 4, 8, 8>"),
             ("hop2_reduce_32way_fp32", "drr", n * (S // 2 + 4 * S // B), 4 * S, "drr_kernel<4, 0, 8, 8>"),
@@ -161,13 +170,13 @@ class Step:
         loc, node = self.local, self.node
         nw = self.W.numel()
 
-        def reorder():
-            z.zpp_reorder_slices(self.bucket, self.reord, 2 * S, n, g)
-
-        def quantize_grad():
-            z.zpp_quantize_blocks(self.reord, z.ZPP_BF16, loc * C, B, 4, self.send1_c, self.send1_s)
-            z.zpp_quantize_blocks(self.reord[loc * C:], z.ZPP_BF16, C, B, 4, self.recv1_c[loc * C // 2:],
-                                  self.recv1_s[loc * C // B:])
+        def reorder_quantize_grad():
+            # slice reorder fused into the one-shot quantize: chunks 0..loc-1 of the
+            # reordered bucket into the send buffer, chunk loc into its receive slot
+            z.zpp_quantize_reordered(self.bucket, z.ZPP_BF16, S, n, g, 0, loc * n, B, 4, self.send1_c,
+                                     self.send1_s)
+            z.zpp_quantize_reordered(self.bucket, z.ZPP_BF16, S, n, g, loc * n, n, B, 4,
+                                     self.recv1_c[loc * C // 2:], self.recv1_s[loc * C // B:])
 
         def hop1():
             z.zpp_dequant_reduce_requant(self.recv1_c, C // 2, self.recv1_s, C // B, g, 4, node * S, B,
@@ -189,7 +198,25 @@ class Step:
         def qg():
             z.zpp_quantize_blocks(self.G, z.ZPP_BF16, nw, 128, 4, self.gc, self.gs)
 
-        return [reorder, quantize_grad, hop1, hop2, qw, dqw, qg]
+        return [reorder_quantize_grad, hop1, hop2, qw, dqw, qg]
+
+    def unfused_launches(self):
+        """The same qgZ first step unfused: the standalone slice reorder of the
+        bf16 bucket, then the quantize of the reordered bucket."""
+        z, c = self.z, self.c
+        n, g, B = c.n_nodes, c.gpus_per_node, c.block
+        S, C = c.slice_len, c.chunk_len
+        loc = self.local
+
+        def reorder():
+            z.zpp_reorder_slices(self.bucket, self.reord, 2 * S, n, g)
+
+        def quantize_reordered_buffer():
+            z.zpp_quantize_blocks(self.reord, z.ZPP_BF16, loc * C, B, 4, self.send1_c, self.send1_s)
+            z.zpp_quantize_blocks(self.reord[loc * C:], z.ZPP_BF16, C, B, 4, self.recv1_c[loc * C // 2:],
+                                  self.recv1_s[loc * C // B:])
+
+        return [reorder, quantize_reordered_buffer]
 
 
 def cpu_baseline(step: "Step", frac: float = 1.0, passes: int = 2):
@@ -327,6 +354,24 @@ def main() -> int:
         "avg_launch_ms": round(ms, 5),
     }
 
+    # the unfused reorder + quantize pair, timed after the steps (not part of them)
+    ufns = step.unfused_launches()
+    for f in ufns:
+        f()
+    uev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ufns]
+           for _ in range(K)]
+    for k in range(K):
+        for i, f in enumerate(ufns):
+            uev[k][i][0].record(stream)
+            f()
+            uev[k][i][1].record(stream)
+    torch.cuda.synchronize()
+    unfused = {}
+    for i, (uname, _, rin_u, wout_u, _) in enumerate(step.unfused_kernels):
+        ms_u = sum(uev[k][i][0].elapsed_time(uev[k][i][1]) for k in range(K)) / K
+        unfused[uname] = {"ms": round(ms_u, 5),
+                          "hbm_frac": round((rin_u + wout_u) / (ms_u * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
@@ -346,8 +391,9 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": ("qgZ 32x8 rank-255 share of a 500M-element bf16 gradient bucket (reorder, int4 "
-                         "B=256 quantize, 8-way hop-1 dequant-reduce-requant, 32-way hop-2 fp32 reduce) + "
+            "workload": ("qgZ 32x8 rank-255 share of a 500M-element bf16 gradient bucket (slice reorder fused "
+                         "into the int4 B=256 quantize, 8-way hop-1 dequant-reduce-requant, 32-way hop-2 fp32 "
+                         "reduce) + "
                          "qwZ/qgZ on one 855,638,016-parameter GQA layer (int8 B=512 quantize and "
                          "dequantize of the weight, int4 B=128 quantize of the gradient)"),
             "bucket_elems": c_bucket(step),
@@ -360,6 +406,7 @@ def main() -> int:
                            "rw_GBps": round((p[2] + p[3]) / (p[5] * 1e-3) / 1e9, 1),
                            "hbm_frac": round((p[2] + p[3]) / (p[5] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
                     for p in per},
+        "unfused_reorder_then_quantize": unfused,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -9,11 +9,11 @@ marshal arguments: every step runs in the library's HIP kernels, and a
 non-OK status raises :class:`ZppError`.
 
 The short helpers (:func:`quantize`, :func:`dequantize`, :func:`reorder`,
-:func:`dequant_reduce_requant`) allocate their outputs with torch on the
+:func:`dequant_reduce_requant`, :func:`quantize_reordered`) allocate their outputs with torch on the
 input's device and call the same entry points.
 
 Importing the package fails with ``ImportError`` when ``libzpp.so`` has not
-been built (``python -m block_quantization_codec_amd._build``); there is no
+been built (``python block_quantization_codec_amd/_build.py``); there is no
 fallback path.
 """
 from __future__ import annotations
@@ -40,7 +40,7 @@ ZPP_MIN_BLOCK = 32
 ZPP_MAX_BLOCK = 4096
 ZPP_MAX_INPUTS = 4096
 
-EXPORTED = ("zpp_quantize_blocks", "zpp_dequantize_blocks", "zpp_reorder_slices",
+EXPORTED = ("zpp_quantize_blocks", "zpp_quantize_reordered", "zpp_dequantize_blocks", "zpp_reorder_slices",
             "zpp_dequant_reduce_requant", "zpp_status_string", "zpp_abi_version")
 
 
@@ -54,11 +54,12 @@ def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: the codec runs only in its HIP library; build it with "
-            "`python -m block_quantization_codec_amd._build` (or __graft_entry__.build())")
+            "`python block_quantization_codec_amd/_build.py` (or __graft_entry__.build())")
     lib = ctypes.CDLL(LIB_PATH)
     P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     sig = {
         "zpp_quantize_blocks": [P, I32, I64, I32, I32, P, P, P],
+        "zpp_quantize_reordered": [P, I32, I64, I32, I32, I32, I32, I32, I32, P, P, P],
         "zpp_dequantize_blocks": [P, P, I32, I64, I32, P, I32, P],
         "zpp_reorder_slices": [P, P, I64, I32, I32, P],
         "zpp_dequant_reduce_requant": [P, I64, P, I64, I32, I32, I64, I32, P, P, I32, P, P],
@@ -113,6 +114,12 @@ def zpp_quantize_blocks(x, x_dtype, numel, block, bits, codes, scales, stream=No
           _stream(stream))
 
 
+def zpp_quantize_reordered(x, x_dtype, slice_elems, n_nodes, gpus_per_node, first_slice, n_slices, block, bits,
+                           codes, scales, stream=None) -> None:
+    _call("zpp_quantize_reordered", _ptr(x), x_dtype, slice_elems, n_nodes, gpus_per_node, first_slice, n_slices,
+          block, bits, _ptr(codes), _ptr(scales), _stream(stream))
+
+
 def zpp_dequantize_blocks(codes, scales, bits, numel, block, y, y_dtype, stream=None) -> None:
     _call("zpp_dequantize_blocks", _ptr(codes), _ptr(scales), bits, numel, block, _ptr(y), y_dtype,
           _stream(stream))
@@ -159,6 +166,26 @@ def quantize(x, block: int, bits: int, stream=None):
     codes = torch.empty(n * bits // 8, dtype=torch.uint8, device=x.device)
     scales = torch.empty(n // block, dtype=torch.float32, device=x.device)
     zpp_quantize_blocks(x, _dtype_code(x), n, block, bits, codes, scales, stream)
+    return codes, scales
+
+
+def quantize_reordered(x, n_nodes: int, gpus_per_node: int, block: int, bits: int, first_slice: int = 0,
+                       n_slices: int | None = None, stream=None):
+    """Quantize the tensor-slice reordered view of contiguous x (N equal slices)
+    without writing the reordered tensor. Returns (codes, scales) of output slices
+    [first_slice, first_slice + n_slices)."""
+    import torch
+
+    n = n_nodes * gpus_per_node
+    if x.numel() % n:
+        raise ValueError("tensor does not split into equal slices")
+    slice_elems = x.numel() // n
+    n_slices = n - first_slice if n_slices is None else n_slices
+    out = slice_elems * n_slices
+    codes = torch.empty(out * bits // 8, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(out // block, dtype=torch.float32, device=x.device)
+    zpp_quantize_reordered(x, _dtype_code(x), slice_elems, n_nodes, gpus_per_node, first_slice, n_slices, block,
+                           bits, codes, scales, stream)
     return codes, scales
 
 

@@ -1,6 +1,7 @@
 """Build ``libzpp.so`` (the HIP codec library) for gfx950 with hipcc, in-tree.
 
-Usage: ``python -m block_quantization_codec_amd._build``. Objects go to
+Usage: ``python block_quantization_codec_amd/_build.py`` (by path: importing
+the package needs the library this builds). Objects go to
 ``_build/`` at the repository root; the library is written next to this file.
 """
 from __future__ import annotations

@@ -42,14 +42,28 @@ struct QuantGeom {
     static constexpr int QMAX = BITS == 8 ? 127 : 7;
 };
 
+// Slices: blockIdx.y is an output slice of `numel` elements. With
+// n_nodes * gpus_per_node > 1 the input is read in QGZ reordered slice order
+// (output slice position p = first_slice + blockIdx.y reads input slice
+// (p % n_nodes) * gpus_per_node + p / n_nodes, see reorder.hip); with one
+// slice and n_nodes = gpus_per_node = 1 this is a plain quantize of x.
 template <int BITS, int LOG2B, bool F32IN>
 __global__ __launch_bounds__(kBlockThreads) void quantize_kernel(const uint8_t *__restrict__ x, int64_t numel,
                                                                  uint8_t *__restrict__ codes,
-                                                                 float *__restrict__ scales) {
+                                                                 float *__restrict__ scales, int n_nodes,
+                                                                 int gpus_per_node, int first_slice) {
     using G = QuantGeom<BITS, LOG2B, F32IN>;
     constexpr int E = G::E, U = G::U, SPB = G::SPB, NB = G::NB;
     constexpr int CW = E * BITS / 32;  // code dwords per lane per segment (E * BITS / 32 >= 1)
 
+    {
+        const int p = first_slice + static_cast<int>(blockIdx.y);
+        const int local = p / n_nodes;
+        const int64_t src = static_cast<int64_t>(p - local * n_nodes) * gpus_per_node + local;
+        x += src * numel * G::IB;
+        codes += static_cast<int64_t>(blockIdx.y) * numel * BITS / 8;
+        scales += static_cast<int64_t>(blockIdx.y) * (numel >> LOG2B);
+    }
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t wave = static_cast<int64_t>(blockIdx.x) * (kBlockThreads / kWave) + (threadIdx.x / kWave);
     const int64_t n_waves = static_cast<int64_t>(gridDim.x) * (kBlockThreads / kWave);
@@ -131,39 +145,61 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_kernel(const uint8_t *
 }
 
 template <int BITS, int LOG2B, bool F32IN>
-hipError_t launch(const void *x, int64_t numel, void *codes, float *scales, hipStream_t stream) {
+hipError_t launch(const void *x, int64_t slice_elems, int n_slices, int n_nodes, int g, int first_slice, void *codes,
+                  float *scales, hipStream_t stream) {
     using G = QuantGeom<BITS, LOG2B, F32IN>;
-    const int64_t tiles = (numel + G::TILE - 1) / G::TILE;
-    const int grid = stream_grid(tiles);
+    const int64_t tiles = (slice_elems + G::TILE - 1) / G::TILE;
+    const dim3 grid(static_cast<unsigned>(stream_grid(tiles)), static_cast<unsigned>(n_slices));
     quantize_kernel<BITS, LOG2B, F32IN><<<grid, kBlockThreads, 0, stream>>>(
-        static_cast<const uint8_t *>(x), numel, static_cast<uint8_t *>(codes), scales);
+        static_cast<const uint8_t *>(x), slice_elems, static_cast<uint8_t *>(codes), scales, n_nodes, g,
+        first_slice);
     return hipGetLastError();
 }
 
+struct QArgs {
+    const void *x;
+    int64_t slice_elems;
+    int n_slices, n_nodes, g, first_slice;
+    void *codes;
+    float *scales;
+    hipStream_t stream;
+};
+
 template <int BITS, bool F32IN>
-hipError_t by_block(int log2b, const void *x, int64_t numel, void *codes, float *scales, hipStream_t st) {
+hipError_t by_block(int log2b, const QArgs &a) {
+#define ZPP_Q(L) launch<BITS, L, F32IN>(a.x, a.slice_elems, a.n_slices, a.n_nodes, a.g, a.first_slice, a.codes, \
+                                        a.scales, a.stream)
     switch (log2b) {
-    case 5: return launch<BITS, 5, F32IN>(x, numel, codes, scales, st);
-    case 6: return launch<BITS, 6, F32IN>(x, numel, codes, scales, st);
-    case 7: return launch<BITS, 7, F32IN>(x, numel, codes, scales, st);
-    case 8: return launch<BITS, 8, F32IN>(x, numel, codes, scales, st);
-    case 9: return launch<BITS, 9, F32IN>(x, numel, codes, scales, st);
-    case 10: return launch<BITS, 10, F32IN>(x, numel, codes, scales, st);
-    case 11: return launch<BITS, 11, F32IN>(x, numel, codes, scales, st);
-    case 12: return launch<BITS, 12, F32IN>(x, numel, codes, scales, st);
+    case 5: return ZPP_Q(5);
+    case 6: return ZPP_Q(6);
+    case 7: return ZPP_Q(7);
+    case 8: return ZPP_Q(8);
+    case 9: return ZPP_Q(9);
+    case 10: return ZPP_Q(10);
+    case 11: return ZPP_Q(11);
+    case 12: return ZPP_Q(12);
     default: return hipErrorInvalidValue;
     }
+#undef ZPP_Q
+}
+
+hipError_t dispatch(bool f32_in, int bits, int log2b, const QArgs &a) {
+    if (bits == 8) return f32_in ? by_block<8, true>(log2b, a) : by_block<8, false>(log2b, a);
+    return f32_in ? by_block<4, true>(log2b, a) : by_block<4, false>(log2b, a);
 }
 
 }  // namespace
 
 hipError_t launch_quantize(const void *x, bool f32_in, int64_t numel, int log2b, int bits, void *codes,
                            float *scales, hipStream_t stream) {
-    if (bits == 8)
-        return f32_in ? by_block<8, true>(log2b, x, numel, codes, scales, stream)
-                      : by_block<8, false>(log2b, x, numel, codes, scales, stream);
-    return f32_in ? by_block<4, true>(log2b, x, numel, codes, scales, stream)
-                  : by_block<4, false>(log2b, x, numel, codes, scales, stream);
+    return dispatch(f32_in, bits, log2b, QArgs{x, numel, 1, 1, 1, 0, codes, scales, stream});
+}
+
+hipError_t launch_quantize_reordered(const void *x, bool f32_in, int64_t slice_elems, int n_nodes, int gpus_per_node,
+                                     int first_slice, int n_slices, int log2b, int bits, void *codes, float *scales,
+                                     hipStream_t stream) {
+    return dispatch(f32_in, bits, log2b,
+                    QArgs{x, slice_elems, n_slices, n_nodes, gpus_per_node, first_slice, codes, scales, stream});
 }
 
 }  // namespace zpp

@@ -19,7 +19,11 @@
 namespace zpp {
 namespace {
 
-constexpr int kU = 4;
+// 16-byte vectors each thread moves per tile.
+#ifndef ZPP_REORDER_VECS
+#define ZPP_REORDER_VECS 1
+#endif
+constexpr int kU = ZPP_REORDER_VECS;
 
 template <int V>
 struct Vec;

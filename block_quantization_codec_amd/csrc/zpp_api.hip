@@ -147,6 +147,31 @@ zpp_status zpp_quantize_blocks(const void *x, zpp_dtype x_dtype, int64_t numel, 
                                          static_cast<hipStream_t>(stream)));
 }
 
+zpp_status zpp_quantize_reordered(const void *x, zpp_dtype x_dtype, int64_t slice_elems, int32_t n_nodes,
+                                  int32_t gpus_per_node, int32_t first_slice, int32_t n_slices, int32_t block,
+                                  int32_t bits, void *codes, float *scales, void *stream) {
+    if (x_dtype != ZPP_BF16 && x_dtype != ZPP_FP32) return ZPP_ERR_ARG;
+    if (bits != 8 && bits != 4) return ZPP_ERR_ARG;
+    if (n_nodes < 1 || gpus_per_node < 1) return ZPP_ERR_ARG;
+    const int64_t n = static_cast<int64_t>(n_nodes) * gpus_per_node;
+    if (n > 65535) return ZPP_ERR_ARG;
+    if (!is_pow2_block(block) || slice_elems < 0 || slice_elems % block != 0) return ZPP_ERR_ARG;
+    if (first_slice < 0 || n_slices < 0 || first_slice + static_cast<int64_t>(n_slices) > n) return ZPP_ERR_ARG;
+    if (slice_elems > (INT64_C(1) << 40) / n) return ZPP_ERR_ARG;
+    if (slice_elems == 0 || n_slices == 0) return ZPP_OK;
+    if (!x || !codes || !scales) return ZPP_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4)) return ZPP_ERR_ALIGN;
+    const int64_t out_elems = slice_elems * n_slices;
+    const Range in{x, n * slice_elems * (x_dtype == ZPP_BF16 ? 2 : 4)}, oc{codes, code_bytes(out_elems, bits)},
+        os{scales, 4 * (out_elems / block)};
+    if (overlap(oc, in) || overlap(os, in) || overlap(oc, os)) return ZPP_ERR_OVERLAP;
+    const Range all[] = {in, oc, os};
+    if (zpp_status s = check_all(all); s != ZPP_OK) return s;
+    return launched(zpp::launch_quantize_reordered(x, x_dtype == ZPP_FP32, slice_elems, n_nodes, gpus_per_node,
+                                                   first_slice, n_slices, log2_of(block), bits, codes, scales,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
 zpp_status zpp_dequantize_blocks(const void *codes, const float *scales, int32_t bits, int64_t numel, int32_t block,
                                  void *y, zpp_dtype y_dtype, void *stream) {
     if (y_dtype != ZPP_BF16 && y_dtype != ZPP_FP32) return ZPP_ERR_ARG;

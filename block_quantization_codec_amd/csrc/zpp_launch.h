@@ -10,6 +10,10 @@ namespace zpp {
 hipError_t launch_quantize(const void *x, bool f32_in, int64_t numel, int log2b, int bits, void *codes,
                            float *scales, hipStream_t stream);
 
+hipError_t launch_quantize_reordered(const void *x, bool f32_in, int64_t slice_elems, int n_nodes, int gpus_per_node,
+                                     int first_slice, int n_slices, int log2b, int bits, void *codes, float *scales,
+                                     hipStream_t stream);
+
 hipError_t launch_dequantize(const void *codes, const float *scales, int bits, int64_t numel, int log2b,
                              void *y, bool f32_out, hipStream_t stream);
 

@@ -104,6 +104,31 @@ zpp_status zpp_quantize_blocks(const void *x, zpp_dtype x_dtype, int64_t numel,
                                void *stream);
 
 /*
+ * Tensor-slice reordering fused into the one-shot quantization [QGZ] (the
+ * page lists kernel fusion among the QGZ optimizations): quantizes the
+ * reordered view of x (see zpp_reorder_slices) without writing it out.
+ * x holds N = n_nodes * gpus_per_node slices of slice_elems elements in
+ * their original order; output slice positions
+ * [first_slice, first_slice + n_slices) of the reordered buffer are
+ * quantized, and their codes and scales are written contiguously, exactly
+ * as zpp_quantize_blocks would write them for those slices of the
+ * reordered buffer (blocks never straddle slices). Choosing the range lets a
+ * caller quantize the chunk it keeps straight into its receive buffer.
+ *
+ *   x               in   N * slice_elems elements of x_dtype, 16-B aligned
+ *   slice_elems     in   multiple of `block`
+ *   n_nodes, gpus_per_node  in  >= 1 each, product <= 65535
+ *   first_slice, n_slices   in  0 <= first_slice, first_slice + n_slices <= N
+ *   block, bits     in   as zpp_quantize_blocks
+ *   codes           out  n_slices * slice_elems * bits / 8 bytes, 16-B aligned
+ *   scales          out  n_slices * slice_elems / block floats, 4-B aligned
+ *   stream          in   hipStream_t
+ */
+zpp_status zpp_quantize_reordered(const void *x, zpp_dtype x_dtype, int64_t slice_elems, int32_t n_nodes,
+                                  int32_t gpus_per_node, int32_t first_slice, int32_t n_slices, int32_t block,
+                                  int32_t bits, void *codes, float *scales, void *stream);
+
+/*
  * Rebuild values from codes and scales: y = code * s_b in binary32, then
  * rounded to nearest-even for ZPP_BF16 output. [QWZ] (the receiver of the
  * 8-bit all-gather needs 16-bit weights to compute with) and [ZPP2].

@@ -18,12 +18,21 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "zpp.h")
 
 
+def _build_module():
+    import importlib.util
+
+    spec = importlib.util.spec_from_file_location(
+        "zpp_build", os.path.join(ROOT, "block_quantization_codec_amd", "_build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
 @pytest.fixture(scope="module")
 def z():
-    from block_quantization_codec_amd import _build
-
-    if _build.stale():
-        _build.build()
+    b = _build_module()
+    if b.stale():
+        b.build()
     import block_quantization_codec_amd as z
 
     return z
@@ -35,9 +44,9 @@ def declared_functions() -> list[str]:
     return sorted(set(re.findall(r"\b(zpp_[a-z0-9_]+)\s*\(", text)))
 
 
-def test_header_declares_the_four_codec_calls():
+def test_header_declares_the_codec_calls():
     names = declared_functions()
-    for n in ("zpp_quantize_blocks", "zpp_dequantize_blocks", "zpp_reorder_slices",
+    for n in ("zpp_quantize_blocks", "zpp_quantize_reordered", "zpp_dequantize_blocks", "zpp_reorder_slices",
               "zpp_dequant_reduce_requant"):
         assert n in names
 
@@ -83,6 +92,32 @@ def test_quantize_argument_errors(z):
     assert q(A, 1, 256, 256, 8, A + 256, A + 8192, None) == z.ZPP_ERR_OVERLAP       # codes in x
     assert q(A, 1, 256, 256, 8, A + 4096, A + 4096 + 128, None) == z.ZPP_ERR_OVERLAP  # scales in codes
     assert q(None, 1, 0, 256, 8, None, None, None) == z.ZPP_OK                        # empty
+
+
+def test_quantize_reordered_argument_errors(z):
+    q = z.library().zpp_quantize_reordered
+    S, O = 1 << 12, A + (1 << 30)
+
+    def call(x=A, dt=1, s=S, n=2, g=4, first=0, count=8, block=256, bits=4, codes=O, scales=O + (1 << 20)):
+        return q(x, dt, s, n, g, first, count, block, bits, codes, scales, None)
+
+    assert call(dt=5) == z.ZPP_ERR_ARG
+    assert call(bits=2) == z.ZPP_ERR_ARG
+    assert call(n=0) == z.ZPP_ERR_ARG
+    assert call(n=256, g=256) == z.ZPP_ERR_ARG                      # more than 65535 slices
+    assert call(s=S + 128) == z.ZPP_ERR_ARG                          # slice not whole blocks
+    assert call(block=48) == z.ZPP_ERR_ARG
+    assert call(first=-1) == z.ZPP_ERR_ARG
+    assert call(first=7, count=2) == z.ZPP_ERR_ARG                  # past the last slice
+    assert call(count=-1) == z.ZPP_ERR_ARG
+    assert call(x=None) == z.ZPP_ERR_NULL
+    assert call(scales=None) == z.ZPP_ERR_NULL
+    assert call(x=A + 8) == z.ZPP_ERR_ALIGN
+    assert call(codes=O + 4) == z.ZPP_ERR_ALIGN
+    assert call(codes=A + 64) == z.ZPP_ERR_OVERLAP                  # codes inside x
+    assert call(scales=O + 64) == z.ZPP_ERR_OVERLAP                 # scales inside codes
+    assert call(x=None, count=0) == z.ZPP_OK                        # nothing to do
+    assert call(x=None, s=0) == z.ZPP_OK
 
 
 def test_dequantize_argument_errors(z):

@@ -221,6 +221,11 @@ def test_qgz_int4_32x8_rank255_chain():
     r2s[node * S // B:].copy_(h1s[node * S // B:(node + 1) * S // B])
     final = torch.empty(S, dtype=torch.float32, device="cuda")
     z.zpp_dequant_reduce_requant(r2c, S // 2, r2s, S // B, n, 4, S, B, None, None, 0, final)
+    # the fused path as the benchmark launches it: chunks 0..6 and chunk 7
+    fc = torch.empty(P // 2, dtype=torch.uint8, device="cuda")
+    fs = torch.empty(P // B, dtype=torch.float32, device="cuda")
+    z.zpp_quantize_reordered(bd, z.ZPP_BF16, S, n, g, 0, local * n, B, 4, fc, fs)
+    z.zpp_quantize_reordered(bd, z.ZPP_BF16, S, n, g, local * n, n, B, 4, fc[local * C // 2:], fs[local * C // B:])
     torch.cuda.synchronize()
 
     _say("compare reorder (complete)")
@@ -231,6 +236,10 @@ def test_qgz_int4_32x8_rank255_chain():
     assert_bits_equal(_rows(codes, B // 2, idx), oc, "codes (sampled)")
     assert_bits_equal(_rows(scales, 1, idx), os_, "scales (sampled)")
     assert_bits_equal(host(codes[local * C // 2:(local + 1) * C // 2]), oq_own[0], "own chunk codes")
+    assert_bits_equal(_rows(fc, B // 2, idx), oc, "fused reorder+quantize codes (sampled)")
+    assert_bits_equal(_rows(fs, 1, idx), os_, "fused reorder+quantize scales (sampled)")
+    assert_bits_equal(host(fc[local * C // 2:]), oq_own[0], "fused own chunk codes")
+    assert_bits_equal(host(fs[local * C // B:]), oq_own[1], "fused own chunk scales")
     _say("compare hop 1 (sampled + own sub-chunk)")
     ins_c = [q[0] for q in oq_peers] + [oq_own[0]]
     ins_s = [q[1] for q in oq_peers] + [oq_own[1]]
