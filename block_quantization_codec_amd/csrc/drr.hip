@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kBlockThreads) void drr_kernel(const uint8_t *__res
     constexpr int U = G::U;
 
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t wave = static_cast<int64_t>(blockIdx.x) * (kBlockThreads / kWave) + (threadIdx.x / kWave);
+    const int64_t wave = xcd_block(blockIdx.x, gridDim.x) * (kBlockThreads / kWave) + (threadIdx.x / kWave);
     const int64_t n_waves = static_cast<int64_t>(gridDim.x) * (kBlockThreads / kWave);
 
     for (int64_t t0 = wave * G::TILE; t0 < numel; t0 += n_waves * G::TILE) {

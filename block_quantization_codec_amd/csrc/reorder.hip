@@ -47,7 +47,7 @@ __global__ __launch_bounds__(kBlockThreads) void reorder_kernel(const uint8_t *_
     const int64_t n_vec = slice_bytes / V;
     constexpr int64_t kTileVec = static_cast<int64_t>(kBlockThreads) * kU;
 
-    for (int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTileVec; t0 < n_vec;
+    for (int64_t t0 = xcd_block(blockIdx.x, gridDim.x) * kTileVec; t0 < n_vec;
          t0 += static_cast<int64_t>(gridDim.x) * kTileVec) {
         T v[kU];
 #pragma unroll

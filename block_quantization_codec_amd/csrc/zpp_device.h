@@ -213,6 +213,23 @@ __device__ __forceinline__ int32_t code_at(uint32_t w, int i) {
 
 // ---- launch geometry --------------------------------------------------------
 
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2).
+// Renumbering them so that each XCD takes one contiguous run of the grid keeps
+// neighbouring tiles, which share cache lines of the small scale arrays, in
+// the same L2. A bijection on [0, grid) for any grid size.
+#ifndef ZPP_XCD_SWIZZLE
+#define ZPP_XCD_SWIZZLE 1
+#endif
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ int64_t xcd_block(int64_t bid, int64_t grid) {
+    if (!ZPP_XCD_SWIZZLE) return bid;
+    const int64_t xcd = bid % kXcds, k = bid / kXcds;
+    const int64_t q = grid / kXcds, r = grid % kXcds;
+    return (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + k;
+}
+
+
 // Workgroups for a grid-stride loop over `tiles` wave-sized tiles: enough to
 // keep every CU of the current device busy, never more than the work needs.
 int stream_grid(int64_t tiles);
