@@ -63,10 +63,10 @@ __global__ __launch_bounds__(kBlockThreads) void dequantize_kernel(const uint8_t
             }
             if constexpr (F32OUT) {
                 uint8_t *dst = y + e0 * 4;
-                st<u32x4>(dst, u32x4{as_u(f[0]), as_u(f[1]), as_u(f[2]), as_u(f[3])});
-                st<u32x4>(dst + 16, u32x4{as_u(f[4]), as_u(f[5]), as_u(f[6]), as_u(f[7])});
+                st_out<u32x4>(dst, u32x4{as_u(f[0]), as_u(f[1]), as_u(f[2]), as_u(f[3])});
+                st_out<u32x4>(dst + 16, u32x4{as_u(f[4]), as_u(f[5]), as_u(f[6]), as_u(f[7])});
             } else {
-                st<u32x4>(y + e0 * 2, u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                st_out<u32x4>(y + e0 * 2, u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
                                             pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])});
             }
         }

@@ -72,12 +72,12 @@ __device__ __forceinline__ void load_dwords(const uint8_t *p, uint32_t (&d)[ND])
 template <int ND>
 __device__ __forceinline__ void store_dwords(uint8_t *p, const uint32_t (&d)[ND]) {
     if constexpr (ND == 1) {
-        st<uint32_t>(p, d[0]);
+        st_out<uint32_t>(p, d[0]);
     } else if constexpr (ND == 2) {
-        st<u32x2>(p, u32x2{d[0], d[1]});
+        st_out<u32x2>(p, u32x2{d[0], d[1]});
     } else {
 #pragma unroll
-        for (int j = 0; j < ND / 4; ++j) st<u32x4>(p + 16 * j, u32x4{d[4 * j], d[4 * j + 1], d[4 * j + 2], d[4 * j + 3]});
+        for (int j = 0; j < ND / 4; ++j) st_out<u32x4>(p + 16 * j, u32x4{d[4 * j], d[4 * j + 1], d[4 * j + 2], d[4 * j + 3]});
     }
 }
 
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(kBlockThreads) void drr_kernel(const uint8_t *__res
                 float *dst = sum_out + e[u];
 #pragma unroll
                 for (int v = 0; v < E / 4; ++v)
-                    st<u32x4>(dst + 4 * v, u32x4{as_u(acc[u][4 * v]), as_u(acc[u][4 * v + 1]),
+                    st_out<u32x4>(dst + 4 * v, u32x4{as_u(acc[u][4 * v]), as_u(acc[u][4 * v + 1]),
                                                  as_u(acc[u][4 * v + 2]), as_u(acc[u][4 * v + 3])});
             }
         }

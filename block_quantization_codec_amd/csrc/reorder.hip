@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kBlockThreads) void reorder_kernel(const uint8_t *_
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             const int64_t i = t0 + u * kBlockThreads + threadIdx.x;
-            if (i < n_vec) st<T>(d + i * V, v[u]);
+            if (i < n_vec) st_out<T>(d + i * V, v[u]);
         }
     }
 }

@@ -45,6 +45,20 @@ template <typename T>
 __device__ __forceinline__ void st_stream(void *p, T v) {
     __builtin_nontemporal_store(v, reinterpret_cast<T *>(p));
 }
+// Bulk outputs (codes, values, sums) are written with streaming stores: an
+// ordinary store leaves dirty lines in L2 and the Infinity Cache that the
+// next kernel then pays to write back, while streaming stores go out to HBM
+// inside the kernel that produced them.
+#ifndef ZPP_STREAM_STORES
+#define ZPP_STREAM_STORES 1
+#endif
+template <typename T>
+__device__ __forceinline__ void st_out(void *p, T v) {
+    if constexpr (ZPP_STREAM_STORES != 0)
+        st_stream<T>(p, v);
+    else
+        st<T>(p, v);
+}
 
 // ---- lane-group maximum of non-negative binary32 bit patterns -------------
 //
