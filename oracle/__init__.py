@@ -53,6 +53,7 @@ def lib():
             "oracle_reorder_slices": [P, P, I64, I32, I32],
             "oracle_dequant_sum": [P, I64, P, I64, I32, I32, I64, I32, P],
             "oracle_dequant_reduce_requant": [P, I64, P, I64, I32, I32, I64, I32, P, P, I32, P],
+            "oracle_dequant_average": [P, I64, P, I64, I32, I32, I64, I32, I32, P],
         }.items():
             f = getattr(L, name)
             f.argtypes = args
@@ -159,6 +160,18 @@ def dequant_reduce_requant(codes_list, scales_list, bits_in: int, numel: int, bl
         numel, block, _ptr(co), _ptr(so), bits_out, _ptr(total))
     _check(rc, "dequant_reduce_requant")
     return co, so, total
+
+
+def dequant_average(codes_list, scales_list, bits: int, numel: int, block: int, divisor: int) -> np.ndarray:
+    """The input-order binary32 sum divided by ``divisor`` (the number of GPUs
+    that contributed), one correctly rounded division per element."""
+    codes = np.stack([np.ascontiguousarray(c, dtype=np.uint8) for c in codes_list])
+    scales = np.stack([np.ascontiguousarray(s, dtype=np.float32) for s in scales_list])
+    out = np.empty(numel, dtype=np.float32)
+    rc = lib().oracle_dequant_average(_ptr(codes), codes.shape[1], _ptr(scales), scales.shape[1],
+                                      len(codes_list), bits, numel, block, divisor, _ptr(out))
+    _check(rc, "dequant_average")
+    return out
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:

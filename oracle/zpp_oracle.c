@@ -24,6 +24,9 @@
  *          parameter shard i.
  *   [ZPP2] "ZeRO-1/2/3" (compassingai concept page), section "ZeRO++":
  *          qwZ weights may be int8 or int4.
+ *   [AVG]  "ZeRO Stage 2: Gradient Partitioning", the numbered steps of the
+ *          stage-2 flow, step 2: the reduce-scatter averages the gradients
+ *          over all GPUs, and GPU i keeps the average for shard i.
  *
  * Readings taken where the pages are silent (each is a choice, not a fact
  * printed on the pages):
@@ -277,6 +280,30 @@ int oracle_dequant_reduce_requant(const uint8_t *codes_in, int64_t codes_stride_
     if (!sum_out)
         free(sum);
     return rc;
+}
+
+/*
+ * [AVG] The reduce-scatter of ZeRO stage 2 hands GPU i the AVERAGED gradient
+ * of shard i. Reading: the average is the binary32 sum above divided by the
+ * number of GPUs that contributed (`divisor`, the data-parallel degree, not
+ * the number of inputs of this hop), one correctly rounded binary32 division
+ * per element.
+ */
+int oracle_dequant_average(const uint8_t *codes_in, int64_t codes_stride_bytes,
+                           const float *scales_in, int64_t scales_stride, int32_t n_inputs,
+                           int32_t bits, int64_t numel, int32_t block, int32_t divisor,
+                           float *avg)
+{
+    if (divisor < 1 || divisor > (1 << 24))
+        return ORACLE_EINVAL;
+    int rc = oracle_dequant_sum(codes_in, codes_stride_bytes, scales_in, scales_stride,
+                                n_inputs, bits, numel, block, avg);
+    if (rc != ORACLE_OK)
+        return rc;
+    const float d = (float)divisor; /* exact: divisor <= 2^24 */
+    for (int64_t i = 0; i < numel; ++i)
+        avg[i] = avg[i] / d;
+    return ORACLE_OK;
 }
 
 /* ---- element conversions exposed for tests ------------------------------ */
