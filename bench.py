@@ -120,6 +120,7 @@ class Step:
         self.recv2_c = torch.empty(n * S // 2, dtype=torch.uint8, device=dev)
         self.recv2_s = torch.empty(n * S // B, dtype=torch.float32, device=dev)
         self.shard = torch.empty(S, dtype=torch.float32, device=dev)
+        self.avg_shard = torch.empty(S, dtype=torch.float32, device=dev)
         # what the exchanges would deliver: peers' chunks and other nodes' pieces
         for i in range(g - 1):
             x = to_dev(c.peer_chunk(i, self.local, self.node))
@@ -147,6 +148,10 @@ class Step:
             ("reorder_bf16_256slices", "reorder", 2 * P, 2 * P, "reorder_kernel<16>"),
             ("quantize_int4_b256_of_reordered", "quantize", 2 * P, P // 2 + 4 * P // B,
              "quantize_kernel<4, 8, false> x2"),
+        ]
+        # the optimizer-ready variant of hop 2 (sum averaged over all n*g GPUs)
+        self.extra_kernels = [
+            ("hop2_average_256gpus_fp32", "drr", n * (S // 2 + 4 * S // B), 4 * S, "drr_kernel<4, 0, 8, 8> (avg)"),
         ]
         self.kernels = [
             ("reorder_quantize_int4_b256", "quantize", 2 * P, P // 2 + 4 * P // B,
@@ -217,6 +222,39 @@ class Step:
                                   self.recv1_s[loc * C // B:])
 
         return [reorder, quantize_reordered_buffer]
+
+
+    def extra_launches(self):
+        """Kernels reported beside the step: hop 2 writing the averaged shard."""
+        z, c = self.z, self.c
+        n, g, B = c.n_nodes, c.gpus_per_node, c.block
+        S = c.slice_len
+
+        def hop2_average():
+            z.zpp_dequant_reduce_average(self.recv2_c, S // 2, self.recv2_s, S // B, n, 4, S, B, n * g,
+                                         self.avg_shard)
+
+        return [hop2_average]
+
+
+def time_rows(torch, stream, fns, table, K):
+    """Average HIP-event time of each callable over K rounds, after one untimed round."""
+    for f in fns:
+        f()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fns]
+          for _ in range(K)]
+    for k in range(K):
+        for i, f in enumerate(fns):
+            ev[k][i][0].record(stream)
+            f()
+            ev[k][i][1].record(stream)
+    torch.cuda.synchronize()
+    out = {}
+    for i, (name, _, rin, wout, _) in enumerate(table):
+        ms = sum(ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(K)) / K
+        out[name] = {"ms": round(ms, 5),
+                     "hbm_frac": round((rin + wout) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    return out
 
 
 def cpu_baseline(step: "Step", frac: float = 1.0, passes: int = 2):
@@ -354,23 +392,10 @@ def main() -> int:
         "avg_launch_ms": round(ms, 5),
     }
 
-    # the unfused reorder + quantize pair, timed after the steps (not part of them)
-    ufns = step.unfused_launches()
-    for f in ufns:
-        f()
-    uev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ufns]
-           for _ in range(K)]
-    for k in range(K):
-        for i, f in enumerate(ufns):
-            uev[k][i][0].record(stream)
-            f()
-            uev[k][i][1].record(stream)
-    torch.cuda.synchronize()
-    unfused = {}
-    for i, (uname, _, rin_u, wout_u, _) in enumerate(step.unfused_kernels):
-        ms_u = sum(uev[k][i][0].elapsed_time(uev[k][i][1]) for k in range(K)) / K
-        unfused[uname] = {"ms": round(ms_u, 5),
-                          "hbm_frac": round((rin_u + wout_u) / (ms_u * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    # timed after the steps, not part of them: the unfused reorder + quantize
+    # pair, and hop 2 writing the averaged (optimizer-ready) shard
+    unfused = time_rows(torch, stream, step.unfused_launches(), step.unfused_kernels, K)
+    extra = time_rows(torch, stream, step.extra_launches(), step.extra_kernels, K)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -407,6 +432,7 @@ def main() -> int:
                            "hbm_frac": round((p[2] + p[3]) / (p[5] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
                     for p in per},
         "unfused_reorder_then_quantize": unfused,
+        "beside_the_step": extra,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -9,7 +9,8 @@ marshal arguments: every step runs in the library's HIP kernels, and a
 non-OK status raises :class:`ZppError`.
 
 The short helpers (:func:`quantize`, :func:`dequantize`, :func:`reorder`,
-:func:`dequant_reduce_requant`, :func:`quantize_reordered`) allocate their outputs with torch on the
+:func:`dequant_reduce_requant`, :func:`dequant_reduce_average`,
+:func:`quantize_reordered`) allocate their outputs with torch on the
 input's device and call the same entry points.
 
 Importing the package fails with ``ImportError`` when ``libzpp.so`` has not
@@ -39,9 +40,10 @@ ZPP_FP32 = 2
 ZPP_MIN_BLOCK = 32
 ZPP_MAX_BLOCK = 4096
 ZPP_MAX_INPUTS = 4096
+ZPP_MAX_DIVISOR = 1 << 24
 
 EXPORTED = ("zpp_quantize_blocks", "zpp_quantize_reordered", "zpp_dequantize_blocks", "zpp_reorder_slices",
-            "zpp_dequant_reduce_requant", "zpp_status_string", "zpp_abi_version")
+            "zpp_dequant_reduce_requant", "zpp_dequant_reduce_average", "zpp_status_string", "zpp_abi_version")
 
 
 class ZppError(RuntimeError):
@@ -63,6 +65,7 @@ def _load() -> ctypes.CDLL:
         "zpp_dequantize_blocks": [P, P, I32, I64, I32, P, I32, P],
         "zpp_reorder_slices": [P, P, I64, I32, I32, P],
         "zpp_dequant_reduce_requant": [P, I64, P, I64, I32, I32, I64, I32, P, P, I32, P, P],
+        "zpp_dequant_reduce_average": [P, I64, P, I64, I32, I32, I64, I32, I32, P, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -134,6 +137,12 @@ def zpp_dequant_reduce_requant(codes_in, codes_stride_bytes, scales_in, scales_s
     _call("zpp_dequant_reduce_requant", _ptr(codes_in), codes_stride_bytes, _ptr(scales_in), scales_stride,
           n_inputs, bits_in, numel, block, _ptr(codes_out), _ptr(scales_out), bits_out, _ptr(sum_out),
           _stream(stream))
+
+
+def zpp_dequant_reduce_average(codes_in, codes_stride_bytes, scales_in, scales_stride, n_inputs, bits_in, numel,
+                               block, divisor, avg_out, stream=None) -> None:
+    _call("zpp_dequant_reduce_average", _ptr(codes_in), codes_stride_bytes, _ptr(scales_in), scales_stride,
+          n_inputs, bits_in, numel, block, divisor, _ptr(avg_out), _stream(stream))
 
 
 def zpp_status_string(status: int) -> str:
@@ -232,3 +241,16 @@ def dequant_reduce_requant(codes_in, scales_in, n_inputs: int, bits_in: int, num
     zpp_dequant_reduce_requant(codes_in, cs, scales_in, ss, n_inputs, bits_in, numel, block, co, so,
                                bits_out, su, stream)
     return co, so, su
+
+
+def dequant_reduce_average(codes_in, scales_in, n_inputs: int, bits_in: int, numel: int, block: int, divisor: int,
+                           codes_stride_bytes: int | None = None, scales_stride: int | None = None, stream=None):
+    """Sum ``n_inputs`` quantized pieces laid side by side and divide by ``divisor``
+    (the number of contributing GPUs). Returns the fp32 average."""
+    import torch
+
+    cs = codes_stride_bytes if codes_stride_bytes is not None else numel * bits_in // 8
+    ss = scales_stride if scales_stride is not None else numel // block
+    avg = torch.empty(numel, dtype=torch.float32, device=codes_in.device)
+    zpp_dequant_reduce_average(codes_in, cs, scales_in, ss, n_inputs, bits_in, numel, block, divisor, avg, stream)
+    return avg

@@ -10,7 +10,10 @@
 //
 // Arithmetic contract: for each element, acc = +0; for r = 0..R-1 in order,
 // acc = fl(acc + fl(code_r * s_r)), every product and every sum rounded on
-// its own, never fused. Scales are non-negative (they are block maxima over
+// its own, never fused. The averaged variant then divides acc by the number
+// of contributing GPUs (one correctly rounded binary32 division): page
+// "ZeRO Stage 2: Gradient Partitioning", step 2 of the stage-2 flow, where
+// the reduce-scatter hands each GPU the average of its shard. Scales are non-negative (they are block maxima over
 // Q), so no product is -0 and +0 + the first product is that product.
 //
 // Layout of the work: a lane owns E consecutive elements of a wave segment of
@@ -167,14 +170,15 @@ __device__ __forceinline__ void sum_batch(const uint8_t *__restrict__ codes_in, 
     }
 }
 
-template <int BITS_IN, int BITS_OUT, int LOG2B, int E>
+template <int BITS_IN, int BITS_OUT, int LOG2B, int E, bool AVG>
 __global__ __launch_bounds__(kBlockThreads) void drr_kernel(const uint8_t *__restrict__ codes_in,
                                                             int64_t codes_stride,
                                                             const float *__restrict__ scales_in,
                                                             int64_t scales_stride, int n_inputs, int64_t numel,
                                                             uint8_t *__restrict__ codes_out,
                                                             float *__restrict__ scales_out,
-                                                            float *__restrict__ sum_out) {
+                                                            float *__restrict__ sum_out, float divisor) {
+    static_assert(!AVG || BITS_OUT == 0, "the average is a final binary32 output");
     using G = DrrGeom<BITS_IN, BITS_OUT, LOG2B, E>;
     constexpr int U = G::U;
 
@@ -207,6 +211,12 @@ __global__ __launch_bounds__(kBlockThreads) void drr_kernel(const uint8_t *__res
         for (; r < n_inputs; ++r)
             sum_batch<G, 1, false>(codes_in, codes_stride, scales_in, scales_stride, r, e, acc);
 
+        if constexpr (AVG) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int i = 0; i < E; ++i) acc[u][i] = acc[u][i] / divisor;  // IEEE division
+        }
         if (sum_out != nullptr) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -242,54 +252,66 @@ __global__ __launch_bounds__(kBlockThreads) void drr_kernel(const uint8_t *__res
     }
 }
 
-template <int BITS_IN, int BITS_OUT, int LOG2B, int E>
-hipError_t launch_e(const void *codes_in, int64_t cstride, const float *scales_in, int64_t sstride, int n_inputs,
-                    int64_t numel, void *codes_out, float *scales_out, float *sum_out, hipStream_t stream) {
+struct DrrArgs {
+    const void *codes_in;
+    int64_t cstride;
+    const float *scales_in;
+    int64_t sstride;
+    int n_inputs;
+    int64_t numel;
+    void *codes_out;
+    float *scales_out;
+    float *sum_out;
+    float divisor;
+    hipStream_t stream;
+};
+
+template <int BITS_IN, int BITS_OUT, int LOG2B, int E, bool AVG>
+hipError_t launch_e(const DrrArgs &a) {
     using G = DrrGeom<BITS_IN, BITS_OUT, LOG2B, E>;
-    const int64_t tiles = (numel + G::TILE - 1) / G::TILE;
-    drr_kernel<BITS_IN, BITS_OUT, LOG2B, E><<<stream_grid(tiles), kBlockThreads, 0, stream>>>(
-        static_cast<const uint8_t *>(codes_in), cstride, scales_in, sstride, n_inputs, numel,
-        static_cast<uint8_t *>(codes_out), scales_out, sum_out);
+    const int64_t tiles = (a.numel + G::TILE - 1) / G::TILE;
+    drr_kernel<BITS_IN, BITS_OUT, LOG2B, E, AVG><<<stream_grid(tiles), kBlockThreads, 0, a.stream>>>(
+        static_cast<const uint8_t *>(a.codes_in), a.cstride, a.scales_in, a.sstride, a.n_inputs, a.numel,
+        static_cast<uint8_t *>(a.codes_out), a.scales_out, a.sum_out, a.divisor);
     return hipGetLastError();
 }
 
-template <int BITS_IN, int BITS_OUT, int LOG2B>
-hipError_t launch(const void *codes_in, int64_t cstride, const float *scales_in, int64_t sstride, int n_inputs,
-                  int64_t numel, void *codes_out, float *scales_out, float *sum_out, hipStream_t stream) {
+template <int BITS_IN, int BITS_OUT, int LOG2B, bool AVG>
+hipError_t launch(const DrrArgs &a) {
     using Wide = DrrGeom<BITS_IN, BITS_OUT, LOG2B, 32>;
-    const int64_t wide_waves = (numel + Wide::TILE - 1) / Wide::TILE;
-    if (wide_waves >= ZPP_DRR_NARROW_WAVES)
-        return launch_e<BITS_IN, BITS_OUT, LOG2B, 32>(codes_in, cstride, scales_in, sstride, n_inputs, numel,
-                                                      codes_out, scales_out, sum_out, stream);
-    return launch_e<BITS_IN, BITS_OUT, LOG2B, 8>(codes_in, cstride, scales_in, sstride, n_inputs, numel, codes_out,
-                                                 scales_out, sum_out, stream);
+    const int64_t wide_waves = (a.numel + Wide::TILE - 1) / Wide::TILE;
+    if (wide_waves >= ZPP_DRR_NARROW_WAVES) return launch_e<BITS_IN, BITS_OUT, LOG2B, 32, AVG>(a);
+    return launch_e<BITS_IN, BITS_OUT, LOG2B, 8, AVG>(a);
 }
 
-template <int BITS_IN, int BITS_OUT>
-hipError_t by_block(int log2b, const void *ci, int64_t cs, const float *si, int64_t ss, int r, int64_t n, void *co,
-                    float *so, float *sum, hipStream_t st) {
+template <int BITS_IN, int BITS_OUT, bool AVG>
+hipError_t by_block(int log2b, const DrrArgs &a) {
     switch (log2b) {
-    case 5: return launch<BITS_IN, BITS_OUT, 5>(ci, cs, si, ss, r, n, co, so, sum, st);
-    case 6: return launch<BITS_IN, BITS_OUT, 6>(ci, cs, si, ss, r, n, co, so, sum, st);
-    case 7: return launch<BITS_IN, BITS_OUT, 7>(ci, cs, si, ss, r, n, co, so, sum, st);
-    case 8: return launch<BITS_IN, BITS_OUT, 8>(ci, cs, si, ss, r, n, co, so, sum, st);
-    case 9: return launch<BITS_IN, BITS_OUT, 9>(ci, cs, si, ss, r, n, co, so, sum, st);
-    case 10: return launch<BITS_IN, BITS_OUT, 10>(ci, cs, si, ss, r, n, co, so, sum, st);
-    case 11: return launch<BITS_IN, BITS_OUT, 11>(ci, cs, si, ss, r, n, co, so, sum, st);
-    case 12: return launch<BITS_IN, BITS_OUT, 12>(ci, cs, si, ss, r, n, co, so, sum, st);
+    case 5: return launch<BITS_IN, BITS_OUT, 5, AVG>(a);
+    case 6: return launch<BITS_IN, BITS_OUT, 6, AVG>(a);
+    case 7: return launch<BITS_IN, BITS_OUT, 7, AVG>(a);
+    case 8: return launch<BITS_IN, BITS_OUT, 8, AVG>(a);
+    case 9: return launch<BITS_IN, BITS_OUT, 9, AVG>(a);
+    case 10: return launch<BITS_IN, BITS_OUT, 10, AVG>(a);
+    case 11: return launch<BITS_IN, BITS_OUT, 11, AVG>(a);
+    case 12: return launch<BITS_IN, BITS_OUT, 12, AVG>(a);
     default: return hipErrorInvalidValue;
     }
 }
 
 template <int BITS_IN>
-hipError_t by_out(int bits_out, int log2b, const void *ci, int64_t cs, const float *si, int64_t ss, int r,
-                  int64_t n, void *co, float *so, float *sum, hipStream_t st) {
+hipError_t by_out(int bits_out, int log2b, const DrrArgs &a) {
     switch (bits_out) {
-    case 0: return by_block<BITS_IN, 0>(log2b, ci, cs, si, ss, r, n, co, so, sum, st);
-    case 4: return by_block<BITS_IN, 4>(log2b, ci, cs, si, ss, r, n, co, so, sum, st);
-    case 8: return by_block<BITS_IN, 8>(log2b, ci, cs, si, ss, r, n, co, so, sum, st);
+    case 0: return a.divisor > 0.0f ? by_block<BITS_IN, 0, true>(log2b, a) : by_block<BITS_IN, 0, false>(log2b, a);
+    case 4: return by_block<BITS_IN, 4, false>(log2b, a);
+    case 8: return by_block<BITS_IN, 8, false>(log2b, a);
     default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t dispatch(int bits_in, int bits_out, int log2b, const DrrArgs &a) {
+    if (bits_in == 8) return by_out<8>(bits_out, log2b, a);
+    return by_out<4>(bits_out, log2b, a);
 }
 
 }  // namespace
@@ -297,11 +319,17 @@ hipError_t by_out(int bits_out, int log2b, const void *ci, int64_t cs, const flo
 hipError_t launch_drr(const void *codes_in, int64_t codes_stride, const float *scales_in, int64_t scales_stride,
                       int n_inputs, int bits_in, int64_t numel, int log2b, void *codes_out, float *scales_out,
                       int bits_out, float *sum_out, hipStream_t stream) {
-    if (bits_in == 8)
-        return by_out<8>(bits_out, log2b, codes_in, codes_stride, scales_in, scales_stride, n_inputs, numel,
-                         codes_out, scales_out, sum_out, stream);
-    return by_out<4>(bits_out, log2b, codes_in, codes_stride, scales_in, scales_stride, n_inputs, numel, codes_out,
-                     scales_out, sum_out, stream);
+    return dispatch(bits_in, bits_out, log2b,
+                    DrrArgs{codes_in, codes_stride, scales_in, scales_stride, n_inputs, numel, codes_out, scales_out,
+                            sum_out, 0.0f, stream});
+}
+
+hipError_t launch_drr_average(const void *codes_in, int64_t codes_stride, const float *scales_in,
+                              int64_t scales_stride, int n_inputs, int bits_in, int64_t numel, int log2b,
+                              int divisor, float *avg_out, hipStream_t stream) {
+    return dispatch(bits_in, 0, log2b,
+                    DrrArgs{codes_in, codes_stride, scales_in, scales_stride, n_inputs, numel, nullptr, nullptr,
+                            avg_out, static_cast<float>(divisor), stream});
 }
 
 }  // namespace zpp

@@ -240,6 +240,29 @@ zpp_status zpp_dequant_reduce_requant(const void *codes_in, int64_t codes_stride
                                     static_cast<hipStream_t>(stream)));
 }
 
+zpp_status zpp_dequant_reduce_average(const void *codes_in, int64_t codes_stride_bytes, const float *scales_in,
+                                      int64_t scales_stride, int32_t n_inputs, int32_t bits_in, int64_t numel,
+                                      int32_t block, int32_t divisor, float *avg_out, void *stream) {
+    if (bits_in != 8 && bits_in != 4) return ZPP_ERR_ARG;
+    if (!is_pow2_block(block) || numel < 0 || numel % block != 0) return ZPP_ERR_ARG;
+    if (n_inputs < 1 || n_inputs > ZPP_MAX_INPUTS) return ZPP_ERR_ARG;
+    if (codes_stride_bytes < 0 || scales_stride < 0) return ZPP_ERR_ARG;
+    if (divisor < 1 || divisor > ZPP_MAX_DIVISOR) return ZPP_ERR_ARG;
+    if (numel == 0) return ZPP_OK;
+    if (!codes_in || !scales_in || !avg_out) return ZPP_ERR_NULL;
+    if (!aligned(codes_in, 16) || (codes_stride_bytes & 15) != 0 || !aligned(scales_in, 4)) return ZPP_ERR_ALIGN;
+    if (!aligned(avg_out, 16)) return ZPP_ERR_ALIGN;
+    const int64_t nblk = numel / block;
+    const Range ic{codes_in, (n_inputs - 1) * codes_stride_bytes + code_bytes(numel, bits_in)},
+        is{scales_in, 4 * ((n_inputs - 1) * scales_stride + nblk)}, ou{avg_out, 4 * numel};
+    if (overlap(ou, ic) || overlap(ou, is)) return ZPP_ERR_OVERLAP;
+    const Range all[] = {ic, is, ou};
+    if (zpp_status s = check_all(all); s != ZPP_OK) return s;
+    return launched(zpp::launch_drr_average(codes_in, codes_stride_bytes, scales_in, scales_stride, n_inputs,
+                                            bits_in, numel, log2_of(block), divisor, avg_out,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 const char *zpp_status_string(zpp_status status) {
     switch (status) {
     case ZPP_OK: return "ZPP_OK";

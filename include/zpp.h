@@ -47,6 +47,9 @@
  *         GPU i holds the reduced gradient of shard i.
  *   [ZPP2] "ZeRO-1/2/3", section "ZeRO++": quantized weights may be 8- or
  *         4-bit.
+ *   [AVG] "ZeRO Stage 2: Gradient Partitioning", the numbered steps of the
+ *         stage-2 flow, step 2: the reduce-scatter averages the gradients
+ *         over all GPUs, and GPU i keeps the average of shard i.
  * Quantization rule (the pages name block quantization but print no
  * formula; this is the symmetric absmax reading the library implements):
  *   a_b = max |x| over block b;  s_b = a_b / Q rounded once to binary32,
@@ -67,6 +70,7 @@ extern "C" {
 #define ZPP_MIN_BLOCK 32
 #define ZPP_MAX_BLOCK 4096
 #define ZPP_MAX_INPUTS 4096
+#define ZPP_MAX_DIVISOR 16777216 /* 2^24: every divisor up to it is exact in binary32 */
 
 typedef enum zpp_status {
     ZPP_OK = 0,
@@ -190,6 +194,25 @@ zpp_status zpp_dequant_reduce_requant(const void *codes_in, int64_t codes_stride
                                       int32_t n_inputs, int32_t bits_in, int64_t numel,
                                       int32_t block, void *codes_out, float *scales_out,
                                       int32_t bits_out, float *sum_out, void *stream);
+
+/*
+ * The final hop of qgZ writing the optimizer-ready shard [QGZ][AVG]: the same
+ * input-order binary32 sum as zpp_dequant_reduce_requant, then divided by
+ * `divisor`, the number of GPUs whose gradients the sum holds (for the
+ * two-hop exchange, n_nodes * gpus_per_node, not n_inputs), with one
+ * correctly rounded binary32 division per element. A power-of-two divisor
+ * only lowers the exponent (exact unless the result is subnormal).
+ *
+ *   codes_in, codes_stride_bytes, scales_in, scales_stride, n_inputs,
+ *   bits_in, numel, block   in   as zpp_dequant_reduce_requant
+ *   divisor             in   1..ZPP_MAX_DIVISOR (1 gives the plain sum)
+ *   avg_out             out  numel floats, 16-B aligned
+ *   stream              in   hipStream_t
+ */
+zpp_status zpp_dequant_reduce_average(const void *codes_in, int64_t codes_stride_bytes,
+                                      const float *scales_in, int64_t scales_stride,
+                                      int32_t n_inputs, int32_t bits_in, int64_t numel,
+                                      int32_t block, int32_t divisor, float *avg_out, void *stream);
 
 /* Static, human-readable name of a status code. Never NULL. */
 const char *zpp_status_string(zpp_status status);

@@ -47,7 +47,7 @@ def declared_functions() -> list[str]:
 def test_header_declares_the_codec_calls():
     names = declared_functions()
     for n in ("zpp_quantize_blocks", "zpp_quantize_reordered", "zpp_dequantize_blocks", "zpp_reorder_slices",
-              "zpp_dequant_reduce_requant"):
+              "zpp_dequant_reduce_requant", "zpp_dequant_reduce_average"):
         assert n in names
 
 
@@ -169,6 +169,32 @@ def test_drr_argument_errors(z):
     assert call(co=C + 64) == z.ZPP_ERR_OVERLAP                                        # output in input
     assert call(so=O + 16) == z.ZPP_ERR_OVERLAP                                        # outputs overlap
     assert call(n=0) == z.ZPP_OK
+
+
+def test_drr_average_argument_errors(z):
+    f = z.library().zpp_dequant_reduce_average
+    C, S, U = A, A + (1 << 24), A + (1 << 27)
+    ok = dict(ci=C, cs=1 << 16, si=S, ss=1 << 10, R=32, bi=4, n=1 << 12, B=256, d=256, av=U)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["ci"], a["cs"], a["si"], a["ss"], a["R"], a["bi"], a["n"], a["B"], a["d"], a["av"], None)
+
+    assert call(bi=0) == z.ZPP_ERR_ARG
+    assert call(R=0) == z.ZPP_ERR_ARG
+    assert call(B=100) == z.ZPP_ERR_ARG
+    assert call(ss=-1) == z.ZPP_ERR_ARG
+    assert call(d=0) == z.ZPP_ERR_ARG
+    assert call(d=-3) == z.ZPP_ERR_ARG
+    assert call(d=z.ZPP_MAX_DIVISOR + 1) == z.ZPP_ERR_ARG
+    assert call(av=None) == z.ZPP_ERR_NULL
+    assert call(si=None) == z.ZPP_ERR_NULL
+    assert call(av=U + 8) == z.ZPP_ERR_ALIGN
+    assert call(cs=24) == z.ZPP_ERR_ALIGN
+    assert call(av=C + 256) == z.ZPP_ERR_OVERLAP
+    assert call(av=S) == z.ZPP_ERR_OVERLAP
+    assert call(n=0) == z.ZPP_OK
+    assert call(n=0, av=None) == z.ZPP_OK
 
 
 def test_oracle_and_library_share_no_code():

@@ -1,4 +1,5 @@
-"""GPU parity of zpp_dequant_reduce_requant against the CPU oracle.
+"""GPU parity of zpp_dequant_reduce_requant and zpp_dequant_reduce_average
+against the CPU oracle.
 
 Codes and scales of the requantized sum must match bit for bit; the binary32
 sum must be within 1e-5 of the largest input scale of its block (and is
@@ -6,7 +7,8 @@ expected bit-exact, both sides adding the same rounded terms in the same
 order). Covers 1..33 inputs (batches of four and remainders), 4- and 8-bit
 inputs and outputs, every block size, strided inputs with gaps, the
 hand-derived golden cases (order of summation, no fused multiply-add), and
-inputs quantized from workload-like data.
+inputs quantized from workload-like data. The averaged variant must match
+the oracle bit for bit for odd, even and power-of-two divisors up to 2^24.
 """
 from __future__ import annotations
 
@@ -188,3 +190,92 @@ def test_wide_lane_path(bits_in, bits_out, R):
     if bits_out:
         assert_bits_equal(gso, so, "scales (wide lanes)")
         assert_bits_equal(gco, co, "codes (wide lanes)")
+
+
+# --------------------------------------------------------------------------
+# zpp_dequant_reduce_average: the hop-2 sum divided by the GPU count
+# --------------------------------------------------------------------------
+
+def _run_avg(codes_np, cstride, scales_np, sstride, R, bits_in, numel, block, divisor):
+    import block_quantization_codec_amd as z
+    ci = dev(codes_np)
+    si = dev(scales_np)
+    ga = Guarded(4 * numel)
+    torch.cuda.synchronize()
+    z.zpp_dequant_reduce_average(ci, cstride, si, sstride, R, bits_in, numel, block, divisor, ga.ptr)
+    torch.cuda.synchronize()
+    assert ga.untouched(), "write outside the output buffer"
+    return ga.as_np(np.float32)
+
+
+def _expect_avg(codes, per_c, scales, per_s, R, bits_in, numel, block, divisor):
+    cl = [codes[r * per_c:r * per_c + numel * bits_in // 8] for r in range(R)]
+    sl = [scales[r * per_s:r * per_s + numel // block] for r in range(R)]
+    return oracle.dequant_average(cl, sl, bits_in, numel, block, divisor)
+
+
+@pytest.mark.parametrize("divisor", [1, 3, 8, 24, 255, 256, 1000, 1 << 24])
+@pytest.mark.parametrize("R,bits_in", [(1, 4), (5, 4), (32, 4), (3, 8), (9, 8)])
+def test_average_matches_oracle(divisor, R, bits_in):
+    block = 256
+    numel = 37 * block  # several tiles and a ragged tail
+    codes, pc, scales, ps = _inputs(R, bits_in, numel, block, 50 + divisor)
+    got = _run_avg(codes, pc, scales, ps, R, bits_in, numel, block, divisor)
+    want = _expect_avg(codes, pc, scales, ps, R, bits_in, numel, block, divisor)
+    assert_bits_equal(got, want, f"average R={R} bits={bits_in} divisor={divisor}")
+
+
+@pytest.mark.parametrize("block", BLOCKS)
+def test_average_block_sizes(block):
+    numel = 3 * 4096 + 2 * block
+    codes, pc, scales, ps = _inputs(6, 4, numel, block, 7, gap=2)
+    got = _run_avg(codes, pc, scales, ps, 6, 4, numel, block, 48)
+    want = _expect_avg(codes, pc, scales, ps, 6, 4, numel, block, 48)
+    assert_bits_equal(got, want, f"average block={block} (strided inputs)")
+
+
+def test_average_wide_lane_path_and_power_of_two():
+    """Large enough for 32 elements per lane; a power-of-two divisor equals the
+    plain sum scaled exactly."""
+    block, R = 256, 4
+    numel = 8192 * 2048 + 7 * block
+    rng = np.random.default_rng([91, R])
+    per_c = numel // 2
+    codes = rng.integers(0, 256, R * per_c, dtype=np.uint8)
+    scales = np.exp2(rng.uniform(-20, -5, R * (numel // block))).astype(np.float32)
+    got = _run_avg(codes, per_c, scales, numel // block, R, 4, numel, block, 3)
+    want = _expect_avg(codes, per_c, scales, numel // block, R, 4, numel, block, 3)
+    assert_bits_equal(got, want, "average (wide lanes), divisor 3")
+    got8 = _run_avg(codes, per_c, scales, numel // block, R, 4, numel, block, 8)
+    _, _, total = _run(codes, per_c, scales, numel // block, R, 4, numel, block, 0)
+    assert_bits_equal(got8, total * np.float32(0.125), "divisor 8 == sum / 8 exactly")
+
+
+def test_golden_average_cases_on_gpu():
+    """Hand-derived cases (blocks of 4) padded with zero codes to a block of 32."""
+    with open(os.path.join(os.path.dirname(__file__), "golden", "average_cases.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        bi, R = c["bits"], len(c["inputs"])
+        codes = np.zeros(R * 32 * bi // 8, np.uint8)
+        scales = np.zeros(R, np.float32)
+        for r, inp in enumerate(c["inputs"]):
+            q = np.zeros(32, np.int64)
+            q[:4] = inp["codes"]
+            codes[r * 32 * bi // 8:(r + 1) * 32 * bi // 8] = _pack(q, bi)
+            scales[r] = inp["scales"][0]
+        got = _run_avg(codes, 32 * bi // 8, scales, 1, R, bi, 32, 32, c["divisor"])
+        if "avg_bits_hex" in c:
+            want = [int(h, 16) for h in c["avg_bits_hex"]]
+            assert got[:4].view(np.uint32).tolist() == want, c["name"]
+        else:
+            assert got[:4].tolist() == c["avg"], c["name"]
+        assert not got[4:].any()
+
+
+def test_average_empty_is_a_no_op():
+    import block_quantization_codec_amd as z
+    g = Guarded(64)
+    z.zpp_dequant_reduce_average(g.ptr, 0, g.ptr, 0, 4, 4, 0, 256, 3, g.ptr)
+    torch.cuda.synchronize()
+    assert g.all_canary()

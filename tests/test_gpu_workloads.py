@@ -221,6 +221,9 @@ def test_qgz_int4_32x8_rank255_chain():
     r2s[node * S // B:].copy_(h1s[node * S // B:(node + 1) * S // B])
     final = torch.empty(S, dtype=torch.float32, device="cuda")
     z.zpp_dequant_reduce_requant(r2c, S // 2, r2s, S // B, n, 4, S, B, None, None, 0, final)
+    # the optimizer-ready shard: the same sum averaged over all n * g GPUs
+    avg = torch.empty(S, dtype=torch.float32, device="cuda")
+    z.zpp_dequant_reduce_average(r2c, S // 2, r2s, S // B, n, 4, S, B, n * g, avg)
     # the fused path as the benchmark launches it: chunks 0..6 and chunk 7
     fc = torch.empty(P // 2, dtype=torch.uint8, device="cuda")
     fs = torch.empty(P // B, dtype=torch.float32, device="cuda")
@@ -258,6 +261,9 @@ def test_qgz_int4_32x8_rank255_chain():
     smax = np.repeat(np.max(np.stack([q[1] for q in oq_parts] + [own_sub[1]]), axis=0), B)
     assert_within_scale(fin, o_fin, smax, "hop-2 sum")
     assert_bits_equal(fin, o_fin, "hop-2 sum bits")
+    o_avg = oracle.dequant_average([q[0] for q in oq_parts] + [own_sub[0]],
+                                   [q[1] for q in oq_parts] + [own_sub[1]], 4, S, B, n * g)
+    assert_bits_equal(host(avg), o_avg, "hop-2 average over 256 GPUs")
     real = c.real_in_slice(rank)
     assert real == 1_913_600 and not fin[real:].any(), "padding must reduce to zero"
 
