@@ -31,6 +31,9 @@ the same work as one step (the reorder and the quantize as two oracle steps),
 twice.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --block-sweep   (one JSON line: quantize / dequantize time
+       and quantization error for every block size 32..4096, 8- and 4-bit codes,
+       on the GQA weight, beside one global scale for the whole tensor)
 """
 from __future__ import annotations
 
@@ -314,12 +317,87 @@ def cpu_baseline(step: "Step", frac: float = 1.0, passes: int = 2):
     }
 
 
+def block_sweep(torch, z, K: int = 10) -> dict:
+    """Kernel time and quantization error for every block size on the GQA weight.
+
+    The error of block quantization is compared with one scale for the whole
+    tensor (global quantization; page "Quantized LLM Training at Scale with
+    ZeRO++", pillar 1 QWZ, credits block quantization with 3.3x better
+    precision than global). Error = root mean square of dequantize(quantize(x)) - x,
+    with the dequantized values from the library in binary32; the global
+    reference is the same rule applied with torch, for comparison only.
+    """
+    import synth
+
+    w = synth.gqa_weight()
+    x = torch.from_numpy(w).view(torch.int16).view(torch.bfloat16).cuda()
+    n = x.numel()
+    stream = torch.cuda.current_stream()
+    chunk = 1 << 26
+
+    def rms_err(y):
+        acc = 0.0
+        for i in range(0, n, chunk):
+            d = y[i:i + chunk].double() - x[i:i + chunk].double()
+            acc += float((d * d).sum())
+        return (acc / n) ** 0.5
+
+    a = x.float().abs().max()
+    rows, global_rms = [], {}
+    y = torch.empty(n, dtype=torch.float32, device="cuda")
+    yb = torch.empty_like(x)
+    for bits in (8, 4):
+        Q = 127.0 if bits == 8 else 7.0
+        sg = (a / Q).float()
+        for i in range(0, n, chunk):
+            xi = x[i:i + chunk].float()
+            y[i:i + chunk] = torch.round(xi / sg).clamp_(-Q, Q) * sg
+        global_rms[str(bits)] = rms_err(y)
+        codes = torch.empty(n * bits // 8, dtype=torch.uint8, device="cuda")
+        for lb in range(5, 13):
+            B = 1 << lb
+            scales = torch.empty(n // B, dtype=torch.float32, device="cuda")
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(2 * K)]
+            z.zpp_quantize_blocks(x, z.ZPP_BF16, n, B, bits, codes, scales)
+            z.zpp_dequantize_blocks(codes, scales, bits, n, B, yb, z.ZPP_BF16)
+            for k in range(K):
+                ev[2 * k][0].record(stream)
+                z.zpp_quantize_blocks(x, z.ZPP_BF16, n, B, bits, codes, scales)
+                ev[2 * k][1].record(stream)
+                ev[2 * k + 1][0].record(stream)
+                z.zpp_dequantize_blocks(codes, scales, bits, n, B, yb, z.ZPP_BF16)
+                ev[2 * k + 1][1].record(stream)
+            torch.cuda.synchronize()
+            qms = sum(ev[2 * k][0].elapsed_time(ev[2 * k][1]) for k in range(K)) / K
+            dms = sum(ev[2 * k + 1][0].elapsed_time(ev[2 * k + 1][1]) for k in range(K)) / K
+            cb, sb = n * bits // 8, 4 * (n // B)
+            z.zpp_dequantize_blocks(codes, scales, bits, n, B, y, z.ZPP_FP32)
+            torch.cuda.synchronize()
+            err = rms_err(y)
+            rows.append({
+                "bits": bits, "block": B,
+                "quantize_ms": round(qms, 4),
+                "quantize_hbm_frac": round((2 * n + cb + sb) / (qms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                "dequantize_ms": round(dms, 4),
+                "dequantize_hbm_frac": round((cb + sb + 2 * n) / (dms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                "rms_error": err,
+                "global_over_block_rms": round(global_rms[str(bits)] / err, 3),
+            })
+            log(f"bits {bits} B {B}: quantize {qms:.3f} ms, dequantize {dms:.3f} ms, rms {err:.3e}")
+            del scales
+        del codes
+    return {"tensor": f"GQA layer weight, {n:,} bf16, N(0, 0.01) with 0.01% outliers x100",
+            "global_rms_error": global_rms, "rows": rows}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    ap.add_argument("--block-sweep", action="store_true",
+                    help="instead of the step: time and error of every block size on the GQA weight")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -337,6 +415,10 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     torch.cuda.set_device(0)
+
+    if args.block_sweep:
+        print(json.dumps({"block_sweep": block_sweep(torch, z)}), flush=True)
+        return 0
 
     # plain copy of known size, for scaling the rocprofv3 byte counters
     cal_src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
