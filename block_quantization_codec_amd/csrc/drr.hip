@@ -32,7 +32,11 @@ namespace {
 #ifndef ZPP_DRR_BATCH
 #define ZPP_DRR_BATCH 8
 #endif
-constexpr int kRB = ZPP_DRR_BATCH;  // inputs per load batch
+// Inputs per load batch of the narrow layout (one code dword and one scale
+// per input and lane; a wave can keep at most 63 loads in flight).
+#ifndef ZPP_DRR_NARROW_BATCH
+#define ZPP_DRR_NARROW_BATCH 16
+#endif
 // Below this many waves at 32 elements per lane, lanes take 8 elements each
 // so that small outputs still spread over every SIMD.
 #ifndef ZPP_DRR_NARROW_WAVES
@@ -52,6 +56,7 @@ struct DrrGeom {
     static constexpr int TILE = U * SEG;
     static constexpr int ND = E * BITS_IN / 32;            // code dwords per lane per input
     static constexpr int QMAX = BITS_OUT == 8 ? 127 : 7;
+    static constexpr int RB = E == 8 ? ZPP_DRR_NARROW_BATCH : ZPP_DRR_BATCH;  // inputs per load batch
 };
 
 template <int ND>
@@ -170,6 +175,21 @@ __device__ __forceinline__ void sum_batch(const uint8_t *__restrict__ codes_in, 
     }
 }
 
+// Sum every remaining full batch of NB inputs from input r on (r advances).
+// r == 0 means no input has been summed yet.
+template <typename G, int NB>
+__device__ __forceinline__ void consume(const uint8_t *__restrict__ codes_in, int64_t codes_stride,
+                                        const float *__restrict__ scales_in, int64_t scales_stride, int n_inputs,
+                                        const int64_t (&e)[G::U], int &r, float (&acc)[G::U][G::E]) {
+    if (r == 0) {
+        if (NB > n_inputs) return;
+        sum_batch<G, NB, true>(codes_in, codes_stride, scales_in, scales_stride, 0, e, acc);
+        r = NB;
+    }
+    for (; r + NB <= n_inputs; r += NB)
+        sum_batch<G, NB, false>(codes_in, codes_stride, scales_in, scales_stride, r, e, acc);
+}
+
 template <int BITS_IN, int BITS_OUT, int LOG2B, int E, bool AVG>
 __global__ __launch_bounds__(kBlockThreads) void drr_kernel(const uint8_t *__restrict__ codes_in,
                                                             int64_t codes_stride,
@@ -198,18 +218,12 @@ __global__ __launch_bounds__(kBlockThreads) void drr_kernel(const uint8_t *__res
 
         float acc[U][E];
         // Inputs are consumed in batches whose loads are all issued before
-        // the batch is summed; the first batch starts the sums.
+        // the batch is summed: full batches of RB, then of 8, then single
+        // inputs; whichever batch comes first starts the sums.
         int r = 0;
-        if (n_inputs >= kRB) {
-            sum_batch<G, kRB, true>(codes_in, codes_stride, scales_in, scales_stride, 0, e, acc);
-            for (r = kRB; r + kRB <= n_inputs; r += kRB)
-                sum_batch<G, kRB, false>(codes_in, codes_stride, scales_in, scales_stride, r, e, acc);
-        } else {
-            sum_batch<G, 1, true>(codes_in, codes_stride, scales_in, scales_stride, 0, e, acc);
-            r = 1;
-        }
-        for (; r < n_inputs; ++r)
-            sum_batch<G, 1, false>(codes_in, codes_stride, scales_in, scales_stride, r, e, acc);
+        consume<G, G::RB>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, e, r, acc);
+        if constexpr (G::RB > 8) consume<G, 8>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, e, r, acc);
+        consume<G, 1>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, e, r, acc);
 
         if constexpr (AVG) {
 #pragma unroll
@@ -230,12 +244,15 @@ __global__ __launch_bounds__(kBlockThreads) void drr_kernel(const uint8_t *__res
         }
 
         if constexpr (BITS_OUT != 0) {
-            uint32_t mx = 0;
+            // |acc| maximum as a float maximum with abs operand modifiers (three
+            // values per instruction); for non-negative finite values it
+            // equals the integer maximum of the bit patterns.
+            float fm = 0.0f;
 #pragma unroll
             for (int u = 0; u < U; ++u)
 #pragma unroll
-                for (int i = 0; i < E; ++i) mx = max(mx, as_u(acc[u][i]) & 0x7FFFFFFFu);
-            if (!ok[0]) mx = 0;
+                for (int i = 0; i < E; ++i) fm = __builtin_fmaxf(fm, __builtin_fabsf(acc[u][i]));
+            uint32_t mx = ok[0] ? as_u(fm) : 0u;
             mx = group_max_u32<G::L>(mx);
             const float sc = block_scale<G::QMAX>(as_f(mx));
 #pragma unroll
