@@ -22,11 +22,12 @@ One step is one pass of the whole per-GPU hot path on resident HBM inputs:
 The peers' hop-1 chunks and the other nodes' hop-2 pieces are drawn from the
 same distributions and quantized once before timing (the exchanges are not
 part of one GPU's work). Reported value: algorithmic input bytes of the six
-kernel rows per step / step time (GB/s). The unfused pair (standalone reorder,
-then quantize of the reordered buffer) is timed after the steps and reported
-beside them. Each kernel is also timed with HIP
-events on the stream it runs on, and the longest one is reported against the
-HBM roofline. The CPU baseline runs the plain C oracle (single thread) over
+kernel rows per step / step time (GB/s), the step timed over K back-to-back
+steps with nothing between the kernels. The same K steps are then run again
+with HIP events around every kernel row on the stream it runs on, and the
+longest row is reported against the HBM roofline. The unfused pair
+(standalone reorder, then quantize of the reordered buffer) and hop 2 writing
+the averaged shard are timed after the steps and reported beside them. The CPU baseline runs the plain C oracle (single thread) over
 the same work as one step (the reorder and the quantize as two oracle steps),
 twice.
 
@@ -436,18 +437,26 @@ def main() -> int:
     torch.cuda.synchronize()
 
     K = args.steps
+    # the step as a caller runs it: K steps back to back, nothing in between
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / K
+
+    # the same K steps again with HIP events around every kernel row
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fns]
           for _ in range(K)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for k in range(K):
         for i, f in enumerate(fns):
             ev[k][i][0].record(stream)
             f()
             ev[k][i][1].record(stream)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / K
 
     per = []
     for i, (name, fam, rin, wout, kname) in enumerate(step.kernels):
