@@ -1,0 +1,106 @@
+"""Argument errors that need the HIP runtime, on real device buffers.
+
+Every entry point must return its status without launching anything: the
+canary bytes around every output stay as they were. Covered here: ordinary
+host memory passed as a device pointer (ZPP_ERR_POINTER), a buffer whose
+byte range runs past its allocation (ZPP_ERR_ARG), misaligned pointers
+(ZPP_ERR_ALIGN) and overlapping buffers (ZPP_ERR_OVERLAP). Pinned host
+memory, which the GPU can address, is accepted as input and gives the same
+result as device memory.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import GUARD, Guarded, assert_bits_equal, dev, host, need_gpu, torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def _z():
+    import block_quantization_codec_amd as z
+    return z
+
+
+def _expect_status(status, fn, *guards):
+    z = _z()
+    with pytest.raises(z.ZppError) as e:
+        fn()
+    assert e.value.status == status, z.zpp_status_string(e.value.status)
+    torch.cuda.synchronize()
+    for g in guards:
+        assert g.all_canary(), "an output was written although the call failed"
+
+
+def test_host_memory_is_rejected_everywhere():
+    z = _z()
+    n, B = 4096, 256
+    host_buf = np.zeros(n * 4, np.uint8)  # ordinary pageable host memory
+    hp = host_buf.ctypes.data
+    x = dev(synth.small_bf16(n, (0, 501), 0.02))
+    sin = torch.ones(2 * n // B, dtype=torch.float32, device="cuda")  # input scales
+    gc, gs, gy = Guarded(n), Guarded(4 * n // B), Guarded(2 * n)
+    P = z.ZPP_ERR_POINTER
+    _expect_status(P, lambda: z.zpp_quantize_blocks(hp, z.ZPP_BF16, n, B, 8, gc.ptr, gs.ptr), gc, gs)
+    _expect_status(P, lambda: z.zpp_quantize_blocks(x, z.ZPP_BF16, n, B, 8, hp, gs.ptr), gs)
+    _expect_status(P, lambda: z.zpp_quantize_reordered(hp, z.ZPP_BF16, n // 4, 2, 2, 0, 4, B, 4, gc.ptr, gs.ptr),
+                   gc, gs)
+    _expect_status(P, lambda: z.zpp_dequantize_blocks(hp, sin, 8, n, B, gy.ptr, z.ZPP_BF16), gy)
+    _expect_status(P, lambda: z.zpp_reorder_slices(hp, gy.ptr, n // 2, 2, 2), gy)
+    _expect_status(P, lambda: z.zpp_dequant_reduce_requant(hp, 0, sin, 0, 2, 8, n, B, gc.ptr, gs.ptr, 8, None),
+                   gc, gs)
+    _expect_status(P, lambda: z.zpp_dequant_reduce_average(hp, 0, sin, 0, 2, 8, n, B, 2, gy.ptr), gy)
+
+
+def test_range_past_the_allocation_is_rejected():
+    """Hop reduction with a stride that carries input 1 a gigabyte past its
+    allocation. The input is the highest of the buffers, so the claimed
+    range cannot overlap an output and only the allocation check can fail."""
+    z = _z()
+    n, B = 1024, 256
+    bufs = [Guarded(4096) for _ in range(3)]
+    bufs.sort(key=lambda g: g.ptr)
+    gc, gs, codes_in = bufs
+    sin = torch.ones(2 * n // B, dtype=torch.float32, device="cuda")  # inputs may overlap each other
+    _expect_status(z.ZPP_ERR_ARG,
+                   lambda: z.zpp_dequant_reduce_requant(codes_in.ptr, 1 << 30, sin, 0, 2, 8, n, B, gc.ptr, gs.ptr,
+                                                        8, None), gc, gs)
+
+
+def test_misaligned_and_overlapping_buffers_are_rejected():
+    z = _z()
+    n, B = 4096, 256
+    x = dev(synth.small_bf16(n, (0, 503), 0.02))
+    gc, gs = Guarded(n + 64), Guarded(4 * n // B + 64)
+    _expect_status(z.ZPP_ERR_ALIGN, lambda: z.zpp_quantize_blocks(x, z.ZPP_BF16, n, B, 8, gc.ptr + 8, gs.ptr),
+                   gc, gs)
+    _expect_status(z.ZPP_ERR_ALIGN, lambda: z.zpp_quantize_blocks(x, z.ZPP_BF16, n, B, 8, gc.ptr, gs.ptr + 2),
+                   gc, gs)
+    _expect_status(z.ZPP_ERR_OVERLAP, lambda: z.zpp_quantize_blocks(x, z.ZPP_BF16, n, B, 8, gc.ptr, gc.ptr + 64),
+                   gc)
+    _expect_status(z.ZPP_ERR_OVERLAP,
+                   lambda: z.zpp_quantize_blocks(x, z.ZPP_BF16, n, B, 8, x.data_ptr(), gs.ptr), gs)
+    assert GUARD >= 64
+
+
+def test_pinned_host_input_is_accepted():
+    z = _z()
+    n, B = 1 << 16, 256
+    xh = torch.from_numpy(synth.small_bf16(n, (0, 504), 0.02, 1e-3, 50.0)).view(torch.int16)
+    pinned = torch.empty(n, dtype=torch.int16, pin_memory=True)
+    pinned.copy_(xh)
+    xd = pinned.cuda()
+    c1 = torch.empty(n, dtype=torch.uint8, device="cuda")
+    s1 = torch.empty(n // B, dtype=torch.float32, device="cuda")
+    z.zpp_quantize_blocks(pinned.data_ptr(), z.ZPP_BF16, n, B, 8, c1, s1)
+    c2, s2 = z.quantize(xd.view(torch.bfloat16), B, 8)
+    torch.cuda.synchronize()
+    assert_bits_equal(host(c1), host(c2), "codes from pinned host input")
+    assert_bits_equal(host(s1), host(s2), "scales from pinned host input")
