@@ -94,6 +94,20 @@ zpp_status check_device_range(Range r) {
         attr.type != hipMemoryTypeUnified)
         return ZPP_ERR_POINTER;
     if (attr.type == hipMemoryTypeHost && attr.devicePointer == nullptr) return ZPP_ERR_POINTER;
+    if (attr.type == hipMemoryTypeDevice) {  // another GPU's memory needs peer access from this one
+        int cur = 0;
+        if (hipGetDevice(&cur) != hipSuccess) {
+            (void)hipGetLastError();
+            return ZPP_ERR_POINTER;
+        }
+        if (attr.device != cur) {
+            int can = 0;
+            if (hipDeviceCanAccessPeer(&can, cur, attr.device) != hipSuccess || !can) {
+                (void)hipGetLastError();
+                return ZPP_ERR_POINTER;
+            }
+        }
+    }
     hipDeviceptr_t base = nullptr;
     size_t size = 0;
     e = hipMemGetAddressRange(&base, &size, const_cast<void *>(r.p));

@@ -11,9 +11,10 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- * - Every data pointer is a DEVICE pointer (memory the GPU can address:
- *   hipMalloc'd, or hipHostMalloc'd pinned host memory). Passing ordinary
- *   host memory is rejected with ZPP_ERR_POINTER.
+ * - Every data pointer is a DEVICE pointer (memory the current GPU can
+ *   address: hipMalloc'd on it or on a peer it can access, or
+ *   hipHostMalloc'd pinned host memory). Ordinary host memory, and another
+ *   GPU's memory without peer access, are rejected with ZPP_ERR_POINTER.
  * - Every call is asynchronous on `stream` (a hipStream_t; NULL means the
  *   null stream). The call validates all arguments on the host first; if any
  *   check fails it returns an error code, launches nothing and leaves every
