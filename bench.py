@@ -56,7 +56,8 @@ KERNEL_SOURCES = {
     "quantize": ["quantize.hip", "zpp_device.h"],
     "dequantize": ["dequantize.hip", "zpp_device.h"],
     "reorder": ["reorder.hip", "zpp_device.h"],
-    "drr": ["drr.hip", "zpp_device.h"],
+    "drr": ["drr.hip", "drr_kernel.h", *(f"drr_in{i}_out{o}.hip" for i in (4, 8) for o in (0, 4, 8)),
+            "zpp_device.h"],
 }
 
 

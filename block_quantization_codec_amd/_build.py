@@ -19,8 +19,9 @@ LIB = os.path.join(PKG, "libzpp.so")
 OBJDIR = os.path.join(ROOT, "_build", "zpp")
 ARCH = os.environ.get("ZPP_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["quantize.hip", "dequantize.hip", "reorder.hip", "drr.hip", "zpp_api.hip"]
-HEADERS = ["zpp_device.h", "zpp_launch.h"]
+DRR_UNITS = [f"drr_in{i}_out{o}.hip" for i in (4, 8) for o in (0, 4, 8)]
+SOURCES = ["quantize.hip", "dequantize.hip", "reorder.hip", "drr.hip", *DRR_UNITS, "zpp_api.hip"]
+HEADERS = ["zpp_device.h", "zpp_launch.h", "drr_kernel.h"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",
@@ -59,8 +60,10 @@ def build(jobs: int | None = None) -> str:
     """Compile every source and link ``libzpp.so``. Always rebuilds."""
     os.makedirs(OBJDIR, exist_ok=True)
     jobs = jobs or max(1, min(len(SOURCES), os.cpu_count() or 1, 16))
+    # the hop-kernel units take longest: start them first
+    order = sorted(SOURCES, key=lambda f: not f.startswith("drr_in"))
     with ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(_compile, order))
     tmp = LIB + f".tmp{os.getpid()}"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -1,334 +1,30 @@
-// drr.hip - fused dequantize -> binary32 reduce -> requantize (the hop step of QGZ).
+// drr.hip - entry of the hop kernels: picks the unit for the code widths.
 //
 // Page "Quantized LLM Training at Scale with ZeRO++", section "The Three
-// Pillars of ZeRO++", pillar 3 (QGZ): the two-hop protocol first exchanges
-// within the node and reduces what arrived, then exchanges across nodes; the
-// page credits kernel fusion among its optimizations. Hop 1 here is
-// dequantize + sum + requantize for the next hop; hop 2 is dequantize + sum
-// into the owner's binary32 shard (page "ZeRO Stage 2: Gradient
-// Partitioning": GPU i keeps shard i, whose optimizer step works in fp32).
-//
-// Arithmetic contract: for each element, acc = +0; for r = 0..R-1 in order,
-// acc = fl(acc + fl(code_r * s_r)), every product and every sum rounded on
-// its own, never fused. The averaged variant then divides acc by the number
-// of contributing GPUs (one correctly rounded binary32 division): page
-// "ZeRO Stage 2: Gradient Partitioning", step 2 of the stage-2 flow, where
-// the reduce-scatter hands each GPU the average of its shard. Scales are non-negative (they are block maxima over
-// Q), so no product is -0 and +0 + the first product is that product.
-//
-// Layout of the work: a lane owns E consecutive elements of a wave segment of
-// 64 E elements: E = 32 (one 16-byte vector of 4-bit codes per input, so
-// each load instruction reads one contiguous kilobyte of an input), or E = 8
-// for small outputs, which then still spread over every SIMD. Inputs are
-// read a batch at a time, all loads of a batch in flight before the batch is
-// summed in input order. The requantized block maximum is reduced across the
-// block's lanes with DPP / permlane swaps.
-#include "zpp_device.h"
-#include "zpp_launch.h"
+// Pillars of ZeRO++", pillar 3 (QGZ): the reduction between the two hops;
+// page "ZeRO Stage 2: Gradient Partitioning": the averaged shard. The kernels
+// themselves are in drr_kernel.h.
+#include "drr_kernel.h"
 
 namespace zpp {
+
 namespace {
 
-#ifndef ZPP_DRR_BATCH
-#define ZPP_DRR_BATCH 8
-#endif
-// Inputs per load batch of the narrow layout (one code dword and one scale
-// per input and lane; a wave can keep at most 63 loads in flight).
-#ifndef ZPP_DRR_NARROW_BATCH
-#define ZPP_DRR_NARROW_BATCH 16
-#endif
-// Below this many waves at 32 elements per lane, lanes take 8 elements each
-// so that small outputs still spread over every SIMD.
-#ifndef ZPP_DRR_NARROW_WAVES
-#define ZPP_DRR_NARROW_WAVES 8192
-#endif
-
-template <int BITS_IN_, int BITS_OUT, int LOG2B_, int E_>
-struct DrrGeom {
-    static constexpr int BITS_IN = BITS_IN_;
-    static constexpr int LOG2B = LOG2B_;
-    static constexpr int E = E_;                           // elements per lane per segment
-    static constexpr int SEG = kWave * E;                  // elements per wave segment
-    static constexpr int B = 1 << LOG2B;
-    static constexpr int SPB = B > SEG ? B / SEG : 1;      // segments per block (= per tile)
-    static constexpr int L = B >= SEG ? kWave : B / E;     // lanes per block within a segment
-    static constexpr int U = SPB;
-    static constexpr int TILE = U * SEG;
-    static constexpr int ND = E * BITS_IN / 32;            // code dwords per lane per input
-    static constexpr int QMAX = BITS_OUT == 8 ? 127 : 7;
-    static constexpr int RB = E == 8 ? ZPP_DRR_NARROW_BATCH : ZPP_DRR_BATCH;  // inputs per load batch
-};
-
-template <int ND>
-__device__ __forceinline__ void load_dwords(const uint8_t *p, uint32_t (&d)[ND]) {
-    if constexpr (ND == 1) {
-        d[0] = ld_stream<uint32_t>(p);
-    } else if constexpr (ND == 2) {
-        const u32x2 v = ld_stream<u32x2>(p);
-        d[0] = v[0];
-        d[1] = v[1];
-    } else {
-#pragma unroll
-        for (int j = 0; j < ND / 4; ++j) {
-            const u32x4 v = ld_stream<u32x4>(p + 16 * j);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) d[4 * j + i] = v[i];
-        }
-    }
-}
-
-template <int ND>
-__device__ __forceinline__ void store_dwords(uint8_t *p, const uint32_t (&d)[ND]) {
-    if constexpr (ND == 1) {
-        st_out<uint32_t>(p, d[0]);
-    } else if constexpr (ND == 2) {
-        st_out<u32x2>(p, u32x2{d[0], d[1]});
-    } else {
-#pragma unroll
-        for (int j = 0; j < ND / 4; ++j) st_out<u32x4>(p + 16 * j, u32x4{d[4 * j], d[4 * j + 1], d[4 * j + 2], d[4 * j + 3]});
-    }
-}
-
-// The codes of dword `w` of one input as binary32 products code * s, element
-// 0 first. FAST (4-bit codes only): a nibble moved to the top of a byte reads
-// as the signed byte 16 * code, and (16 * code) * (s / 16) is the same real
-// product as code * s, so it rounds identically whenever s / 16 is exact
-// (s == 0 or s >= 2^-122). 8-bit codes convert directly.
-template <int BITS_IN, bool FAST>
-__device__ __forceinline__ void dequant_dword(uint32_t w, float s, float s16, float (&p)[32 / BITS_IN]) {
-    if constexpr (BITS_IN == 8) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = static_cast<float>(static_cast<int8_t>(w >> (8 * i))) * s;
-    } else if constexpr (FAST) {
-        const uint32_t even = (w << 4) & 0xF0F0F0F0u;  // byte i: code 2i << 4
-        const uint32_t odd = w & 0xF0F0F0F0u;          // byte i: code 2i+1 << 4
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            p[2 * i] = static_cast<float>(static_cast<int8_t>(even >> (8 * i))) * s16;
-            p[2 * i + 1] = static_cast<float>(static_cast<int8_t>(odd >> (8 * i))) * s16;
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) p[i] = static_cast<float>(code_at<4>(w, i)) * s;
-    }
-}
-
-// Sum one batch of loaded inputs into acc, in input order.
-template <typename G, int NB, bool FIRST, bool FAST>
-__device__ __forceinline__ void accumulate(const uint32_t (&w)[NB][G::U][G::ND], const float (&s)[NB][G::U],
-                                           float (&acc)[G::U][G::E]) {
-    constexpr int CPW = 32 / G::BITS_IN;  // codes per dword
-#pragma unroll
-    for (int k = 0; k < NB; ++k) {
-#pragma unroll
-        for (int u = 0; u < G::U; ++u) {
-            const float sk = s[k][u];
-            const float s16 = sk * 0.0625f;
-#pragma unroll
-            for (int d = 0; d < G::ND; ++d) {
-                float p[CPW];
-                dequant_dword<G::BITS_IN, FAST>(w[k][u][d], sk, s16, p);
-#pragma unroll
-                for (int i = 0; i < CPW; ++i) {
-                    if (FIRST && k == 0)
-                        acc[u][d * CPW + i] = p[i];
-                    else
-                        acc[u][d * CPW + i] = acc[u][d * CPW + i] + p[i];
-                }
-            }
-        }
-    }
-}
-
-// Add inputs r0 .. r0+NB-1 (in that order) into acc. FIRST: input r0 starts
-// the sums: acc = +0 + p, where p is never -0 (a zero code gives +0 for a
-// non-negative scale), so acc = p.
-template <typename G, int NB, bool FIRST>
-__device__ __forceinline__ void sum_batch(const uint8_t *__restrict__ codes_in, int64_t codes_stride,
-                                          const float *__restrict__ scales_in, int64_t scales_stride, int r0,
-                                          const int64_t (&e)[G::U], float (&acc)[G::U][G::E]) {
-    constexpr int U = G::U, BITS_IN = G::BITS_IN;
-    uint32_t w[NB][U][G::ND];
-    float s[NB][U];
-#pragma unroll
-    for (int k = 0; k < NB; ++k) {
-        const uint8_t *c = codes_in + static_cast<int64_t>(r0 + k) * codes_stride;
-        const float *sc = scales_in + static_cast<int64_t>(r0 + k) * scales_stride;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            load_dwords<G::ND>(c + e[u] * BITS_IN / 8, w[k][u]);
-            s[k][u] = sc[e[u] >> G::LOG2B];
-        }
-    }
-    if constexpr (BITS_IN == 8) {
-        accumulate<G, NB, FIRST, true>(w, s, acc);
-    } else {
-        bool fast = true;
-#pragma unroll
-        for (int k = 0; k < NB; ++k)
-#pragma unroll
-            for (int u = 0; u < U; ++u) fast &= (s[k][u] == 0.0f) | (s[k][u] >= 0x1p-122f);
-        if (fast)
-            accumulate<G, NB, FIRST, true>(w, s, acc);
-        else
-            accumulate<G, NB, FIRST, false>(w, s, acc);
-    }
-}
-
-// Sum every remaining full batch of NB inputs from input r on (r advances).
-// r == 0 means no input has been summed yet.
-template <typename G, int NB>
-__device__ __forceinline__ void consume(const uint8_t *__restrict__ codes_in, int64_t codes_stride,
-                                        const float *__restrict__ scales_in, int64_t scales_stride, int n_inputs,
-                                        const int64_t (&e)[G::U], int &r, float (&acc)[G::U][G::E]) {
-    if (r == 0) {
-        if (NB > n_inputs) return;
-        sum_batch<G, NB, true>(codes_in, codes_stride, scales_in, scales_stride, 0, e, acc);
-        r = NB;
-    }
-    for (; r + NB <= n_inputs; r += NB)
-        sum_batch<G, NB, false>(codes_in, codes_stride, scales_in, scales_stride, r, e, acc);
-}
-
-template <int BITS_IN, int BITS_OUT, int LOG2B, int E, bool AVG>
-__global__ __launch_bounds__(kBlockThreads) void drr_kernel(const uint8_t *__restrict__ codes_in,
-                                                            int64_t codes_stride,
-                                                            const float *__restrict__ scales_in,
-                                                            int64_t scales_stride, int n_inputs, int64_t numel,
-                                                            uint8_t *__restrict__ codes_out,
-                                                            float *__restrict__ scales_out,
-                                                            float *__restrict__ sum_out, float divisor) {
-    static_assert(!AVG || BITS_OUT == 0, "the average is a final binary32 output");
-    using G = DrrGeom<BITS_IN, BITS_OUT, LOG2B, E>;
-    constexpr int U = G::U;
-
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t wave = xcd_block(blockIdx.x, gridDim.x) * (kBlockThreads / kWave) + (threadIdx.x / kWave);
-    const int64_t n_waves = static_cast<int64_t>(gridDim.x) * (kBlockThreads / kWave);
-
-    for (int64_t t0 = wave * G::TILE; t0 < numel; t0 += n_waves * G::TILE) {
-        int64_t e[U];
-        bool ok[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t e0 = t0 + static_cast<int64_t>(u) * G::SEG + lane * E;
-            ok[u] = e0 < numel;
-            e[u] = ok[u] ? e0 : 0;
-        }
-
-        float acc[U][E];
-        // Inputs are consumed in batches whose loads are all issued before
-        // the batch is summed: full batches of RB, then of 8, then single
-        // inputs; whichever batch comes first starts the sums.
-        int r = 0;
-        consume<G, G::RB>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, e, r, acc);
-        if constexpr (G::RB > 8) consume<G, 8>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, e, r, acc);
-        consume<G, 1>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, e, r, acc);
-
-        if constexpr (AVG) {
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-#pragma unroll
-                for (int i = 0; i < E; ++i) acc[u][i] = acc[u][i] / divisor;  // IEEE division
-        }
-        if (sum_out != nullptr) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                if (!ok[u]) continue;
-                float *dst = sum_out + e[u];
-#pragma unroll
-                for (int v = 0; v < E / 4; ++v)
-                    st_out<u32x4>(dst + 4 * v, u32x4{as_u(acc[u][4 * v]), as_u(acc[u][4 * v + 1]),
-                                                 as_u(acc[u][4 * v + 2]), as_u(acc[u][4 * v + 3])});
-            }
-        }
-
-        if constexpr (BITS_OUT != 0) {
-            // |acc| maximum as a float maximum with abs operand modifiers (three
-            // values per instruction); for non-negative finite values it
-            // equals the integer maximum of the bit patterns.
-            float fm = 0.0f;
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-#pragma unroll
-                for (int i = 0; i < E; ++i) fm = __builtin_fmaxf(fm, __builtin_fabsf(acc[u][i]));
-            uint32_t mx = ok[0] ? as_u(fm) : 0u;
-            mx = group_max_u32<G::L>(mx);
-            const float sc = block_scale<G::QMAX>(as_f(mx));
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float mg[E];
-                round_codes<E, BITS_OUT>(acc[u], sc, mg);
-                uint32_t cw[E * BITS_OUT / 32];
-                pack_codes<E, BITS_OUT>(mg, cw);
-                if (!ok[u]) continue;
-                store_dwords<E * BITS_OUT / 32>(codes_out + e[u] * BITS_OUT / 8, cw);
-                if (u == 0 && (lane & (G::L - 1)) == 0) scales_out[e[u] >> LOG2B] = sc;
-            }
-        }
-    }
-}
-
-struct DrrArgs {
-    const void *codes_in;
-    int64_t cstride;
-    const float *scales_in;
-    int64_t sstride;
-    int n_inputs;
-    int64_t numel;
-    void *codes_out;
-    float *scales_out;
-    float *sum_out;
-    float divisor;
-    hipStream_t stream;
-};
-
-template <int BITS_IN, int BITS_OUT, int LOG2B, int E, bool AVG>
-hipError_t launch_e(const DrrArgs &a) {
-    using G = DrrGeom<BITS_IN, BITS_OUT, LOG2B, E>;
-    const int64_t tiles = (a.numel + G::TILE - 1) / G::TILE;
-    drr_kernel<BITS_IN, BITS_OUT, LOG2B, E, AVG><<<stream_grid(tiles), kBlockThreads, 0, a.stream>>>(
-        static_cast<const uint8_t *>(a.codes_in), a.cstride, a.scales_in, a.sstride, a.n_inputs, a.numel,
-        static_cast<uint8_t *>(a.codes_out), a.scales_out, a.sum_out, a.divisor);
-    return hipGetLastError();
-}
-
-template <int BITS_IN, int BITS_OUT, int LOG2B, bool AVG>
-hipError_t launch(const DrrArgs &a) {
-    using Wide = DrrGeom<BITS_IN, BITS_OUT, LOG2B, 32>;
-    const int64_t wide_waves = (a.numel + Wide::TILE - 1) / Wide::TILE;
-    if (wide_waves >= ZPP_DRR_NARROW_WAVES) return launch_e<BITS_IN, BITS_OUT, LOG2B, 32, AVG>(a);
-    return launch_e<BITS_IN, BITS_OUT, LOG2B, 8, AVG>(a);
-}
-
-template <int BITS_IN, int BITS_OUT, bool AVG>
-hipError_t by_block(int log2b, const DrrArgs &a) {
-    switch (log2b) {
-    case 5: return launch<BITS_IN, BITS_OUT, 5, AVG>(a);
-    case 6: return launch<BITS_IN, BITS_OUT, 6, AVG>(a);
-    case 7: return launch<BITS_IN, BITS_OUT, 7, AVG>(a);
-    case 8: return launch<BITS_IN, BITS_OUT, 8, AVG>(a);
-    case 9: return launch<BITS_IN, BITS_OUT, 9, AVG>(a);
-    case 10: return launch<BITS_IN, BITS_OUT, 10, AVG>(a);
-    case 11: return launch<BITS_IN, BITS_OUT, 11, AVG>(a);
-    case 12: return launch<BITS_IN, BITS_OUT, 12, AVG>(a);
-    default: return hipErrorInvalidValue;
-    }
-}
-
-template <int BITS_IN>
-hipError_t by_out(int bits_out, int log2b, const DrrArgs &a) {
-    switch (bits_out) {
-    case 0: return a.divisor > 0.0f ? by_block<BITS_IN, 0, true>(log2b, a) : by_block<BITS_IN, 0, false>(log2b, a);
-    case 4: return by_block<BITS_IN, 4, false>(log2b, a);
-    case 8: return by_block<BITS_IN, 8, false>(log2b, a);
-    default: return hipErrorInvalidValue;
-    }
-}
-
 hipError_t dispatch(int bits_in, int bits_out, int log2b, const DrrArgs &a) {
-    if (bits_in == 8) return by_out<8>(bits_out, log2b, a);
-    return by_out<4>(bits_out, log2b, a);
+    if (bits_in == 8) {
+        switch (bits_out) {
+        case 0: return drr_dispatch_in8_out0(log2b, a);
+        case 4: return drr_dispatch_in8_out4(log2b, a);
+        case 8: return drr_dispatch_in8_out8(log2b, a);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    switch (bits_out) {
+    case 0: return drr_dispatch_in4_out0(log2b, a);
+    case 4: return drr_dispatch_in4_out4(log2b, a);
+    case 8: return drr_dispatch_in4_out8(log2b, a);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace

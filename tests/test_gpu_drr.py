@@ -279,3 +279,33 @@ def test_average_empty_is_a_no_op():
     z.zpp_dequant_reduce_average(g.ptr, 0, g.ptr, 0, 4, 4, 0, 256, 3, g.ptr)
     torch.cuda.synchronize()
     assert g.all_canary()
+
+
+@pytest.mark.parametrize("bits_in", [4, 8])
+@pytest.mark.parametrize("R", [1, 2, 9, 17])
+def test_zero_and_negative_scales_with_negative_codes(bits_in, R):
+    """Negative codes with zero (or negative) scales give -0 products. The sum
+    starts from +0 and adds every product, so where all products of an element
+    are -0 the result is +0 (+0 + -0 = +0), and the requantized block is all
+    zero. Arbitrary code bytes and scales are accepted by the entry point."""
+    block = 64
+    numel = 40 * block
+    per_c = numel * bits_in // 8
+    rng = np.random.default_rng([77, bits_in, R])
+    codes = rng.integers(0, 256, R * per_c, dtype=np.uint8)
+    nb = numel // block
+    scales = np.exp2(rng.uniform(-20, -5, R * nb)).astype(np.float32)
+    scales[rng.random(R * nb) < 0.5] = 0.0          # zero scales in about half the blocks
+    scales[rng.random(R * nb) < 0.1] *= -1.0        # and a few negative ones
+    scales[:nb] = np.where(np.arange(nb) % 3 == 0, np.float32(0.0), scales[:nb])
+    for bits_out in (0, 4, 8):
+        gco, gso, gsu = _run(codes, per_c, scales, nb, R, bits_in, numel, block, bits_out)
+        cl = [codes[r * per_c:(r + 1) * per_c] for r in range(R)]
+        sl = [scales[r * nb:(r + 1) * nb] for r in range(R)]
+        co, so, su = oracle.dequant_reduce_requant(cl, sl, bits_in, numel, block, bits_out)
+        assert_bits_equal(gsu, su, f"sum with zero/negative scales, bits_out={bits_out}")
+        if bits_out:
+            assert_bits_equal(gso, so, "requantized scales")
+            assert_bits_equal(gco, co, "requantized codes")
+    avg = _run_avg(codes, per_c, scales, nb, R, bits_in, numel, block, 3)
+    assert_bits_equal(avg, oracle.dequant_average(cl, sl, bits_in, numel, block, 3), "average")
