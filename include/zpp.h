@@ -189,6 +189,10 @@ zpp_status zpp_reorder_slices(const void *in, void *out, int64_t slice_bytes, in
  *   sum_out             out  binary32 sum (numel floats, 16-B aligned), or NULL
  *   stream              in   hipStream_t
  * At least one of the two outputs must be requested (ZPP_ERR_ARG).
+ * Any code bytes and any finite scales are accepted; the binary32 sum is
+ * exact to the contract for all of them. A sum that overflows to infinity
+ * (only possible with scales near the binary32 limit) is outside the
+ * contract for requantization: that block's codes and scale are unspecified.
  */
 zpp_status zpp_dequant_reduce_requant(const void *codes_in, int64_t codes_stride_bytes,
                                       const float *scales_in, int64_t scales_stride,
