@@ -60,6 +60,8 @@ hipError_t drr_dispatch_in8_out8(int log2b, const DrrArgs &a);
 
 namespace {
 
+// Inputs per load batch of the wide layout (a 16-byte code vector and one
+// scale per input and lane).
 #ifndef ZPP_DRR_BATCH
 #define ZPP_DRR_BATCH 8
 #endif

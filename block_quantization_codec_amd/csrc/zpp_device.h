@@ -1,11 +1,11 @@
 // zpp_device.h - device helpers shared by the codec kernels (gfx950 / CDNA4, wave64).
 //
-// Internal to the library. Every kernel streams HBM with 16-byte vector
-// accesses that are contiguous across the 64 lanes of a wave (streaming
-// inputs are read with non-temporal loads), reduces block maxima across lanes
-// with DPP row operations and the gfx950 permlane swaps (no LDS traffic), and
-// keeps all arithmetic in binary32 with fp contraction off, so every product
-// and sum is rounded on its own.
+// Internal to the library. Every kernel streams HBM with vector accesses
+// that are contiguous across the 64 lanes of a wave (inputs read once with
+// non-temporal loads, bulk outputs written with streaming stores), reduces
+// block maxima across lanes with DPP row operations and the gfx950 permlane
+// swaps (no LDS traffic), and keeps all arithmetic in binary32 with fp
+// contraction off, so every product and sum is rounded on its own.
 #pragma once
 
 #include <hip/hip_runtime.h>
