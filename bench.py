@@ -25,9 +25,11 @@ part of one GPU's work). Reported value: algorithmic input bytes of the six
 kernel rows per step / step time (GB/s), the step timed over K back-to-back
 steps with nothing between the kernels. The same K steps are then run again
 with HIP events around every kernel row on the stream it runs on, and the
-longest row is reported against the HBM roofline. The unfused pair
-(standalone reorder, then quantize of the reordered buffer) and hop 2 writing
-the averaged shard are timed after the steps and reported beside them. The CPU baseline runs the plain C oracle (single thread) over
+longest row is reported against the HBM roofline. Timed after the steps and
+reported beside them: the unfused pair (standalone reorder of the bf16
+bucket, then quantize of the reordered buffer), the other unfused order
+(quantize the bucket as it is, then reorder its codes and scales), and hop 2
+writing the averaged shard. The CPU baseline runs the plain C oracle (single thread) over
 the same work as one step (the reorder and the quantize as two oracle steps),
 twice.
 
@@ -126,6 +128,10 @@ class Step:
         self.recv2_s = torch.empty(n * S // B, dtype=torch.float32, device=dev)
         self.shard = torch.empty(S, dtype=torch.float32, device=dev)
         self.avg_shard = torch.empty(S, dtype=torch.float32, device=dev)
+        self.pre_c = torch.empty(P // 2, dtype=torch.uint8, device=dev)      # codes before the reorder
+        self.pre_s = torch.empty(P // B, dtype=torch.float32, device=dev)
+        self.post_c = torch.empty(P // 2, dtype=torch.uint8, device=dev)     # and after it
+        self.post_s = torch.empty(P // B, dtype=torch.float32, device=dev)
         # what the exchanges would deliver: peers' chunks and other nodes' pieces
         for i in range(g - 1):
             x = to_dev(c.peer_chunk(i, self.local, self.node))
@@ -154,9 +160,15 @@ class Step:
             ("quantize_int4_b256_of_reordered", "quantize", 2 * P, P // 2 + 4 * P // B,
              "quantize_kernel<4, 8, false> x2"),
         ]
-        # the optimizer-ready variant of hop 2 (sum averaged over all n*g GPUs)
+        # beside the step: the optimizer-ready variant of hop 2 (sum averaged over
+        # all n*g GPUs), and the other unfused order of rows a3/a4 (quantize the
+        # bucket as it is, then reorder its codes and scales)
         self.extra_kernels = [
             ("hop2_average_256gpus_fp32", "drr", n * (S // 2 + 4 * S // B), 4 * S, "drr_kernel<4, 0, 8, 8> (avg)"),
+            ("quantize_int4_b256_before_reorder", "quantize", 2 * P, P // 2 + 4 * P // B,
+             "quantize_kernel<4, 8, false>"),
+            ("reorder_int4_codes_and_scales", "reorder", P // 2 + 4 * P // B, P // 2 + 4 * P // B,
+             "reorder_kernel<16> + reorder_kernel<8>"),
         ]
         self.kernels = [
             ("reorder_quantize_int4_b256", "quantize", 2 * P, P // 2 + 4 * P // B,
@@ -239,7 +251,14 @@ class Step:
             z.zpp_dequant_reduce_average(self.recv2_c, S // 2, self.recv2_s, S // B, n, 4, S, B, n * g,
                                          self.avg_shard)
 
-        return [hop2_average]
+        def quantize_before_reorder():
+            z.zpp_quantize_blocks(self.bucket, z.ZPP_BF16, n * g * S, B, 4, self.pre_c, self.pre_s)
+
+        def reorder_codes_and_scales():
+            z.zpp_reorder_slices(self.pre_c, self.post_c, S // 2, n, g)
+            z.zpp_reorder_slices(self.pre_s, self.post_s, 4 * S // B, n, g)
+
+        return [hop2_average, quantize_before_reorder, reorder_codes_and_scales]
 
 
 def time_rows(torch, stream, fns, table, K):

@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
+import synth
 from gpu_util import Guarded, assert_bits_equal, dev, need_gpu, torch
 
 pytestmark = pytest.mark.gpu
@@ -73,3 +74,19 @@ def test_reorder_of_codes_and_scales_at_32x8_slice_shape():
 def test_zero_slices_are_a_no_op():
     import block_quantization_codec_amd as z
     z.zpp_reorder_slices(None, None, 0, 2, 4)
+
+
+def test_reorder_of_full_size_codes_and_scales_at_32x8():
+    """The other unfused order of the 500M-element bucket at 32x8: its 4-bit
+    codes (256 slices of 976,640 bytes) and scales (256 slices of 30,520 bytes,
+    which take the 8-byte vector path) reordered as the benchmark does it,
+    compared with the oracle's reorder in full."""
+    n, g = 32, 8
+    S = synth.QGZ_INT4_32x8.slice_len
+    B = synth.QGZ_INT4_32x8.block
+    N = n * g
+    rng = np.random.default_rng(17)
+    codes = rng.integers(0, 256, N * S // 2, dtype=np.uint8)
+    scales = rng.integers(0, 256, N * 4 * S // B, dtype=np.uint8)
+    assert_bits_equal(_run(codes, S // 2, n, g), oracle.reorder_slices(codes, n, g), "codes at 32x8")
+    assert_bits_equal(_run(scales, 4 * S // B, n, g), oracle.reorder_slices(scales, n, g), "scales at 32x8")
