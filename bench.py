@@ -478,10 +478,13 @@ def main() -> int:
             ev[k][i][1].record(stream)
     torch.cuda.synchronize()
 
-    per = []
+    per, spread = [], {}
     for i, (name, fam, rin, wout, kname) in enumerate(step.kernels):
-        ms = sum(ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(K)) / K
+        times = sorted(ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(K))
+        ms = sum(times) / K
         per.append((name, fam, rin, wout, kname, ms))
+        spread[name] = {"ms_p10": round(times[int(0.1 * (K - 1))], 5), "ms_p50": round(times[(K - 1) // 2], 5),
+                        "ms_p90": round(times[int(0.9 * (K - 1) + 0.5)], 5)}
     total_in = sum(p[2] for p in per)
     total_rw = sum(p[2] + p[3] for p in per)
     value = total_in / (ms_per_step * 1e-3) / 1e9
@@ -538,7 +541,7 @@ def main() -> int:
             "parallelism": "none (one GPU's share of ZeRO++ data parallelism)",
         },
         "hbm_frac_step": round(total_rw / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-        "kernels": {p[0]: {"ms": round(p[5], 5), "in_GBps": round(p[2] / (p[5] * 1e-3) / 1e9, 1),
+        "kernels": {p[0]: {"ms": round(p[5], 5), **spread[p[0]], "in_GBps": round(p[2] / (p[5] * 1e-3) / 1e9, 1),
                            "rw_GBps": round((p[2] + p[3]) / (p[5] * 1e-3) / 1e9, 1),
                            "hbm_frac": round((p[2] + p[3]) / (p[5] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
                     for p in per},
