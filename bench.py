@@ -333,9 +333,22 @@ def cpu_baseline(step: "Step", frac: float = 1.0, passes: int = 2):
                    f"({sub_s}-element slices, {hop_n}-element hop-1 chunk, {w_n}/{g_n} GQA elements), "
                    f"{passes} passes: {total_in / 1e9:.2f} GB of input in {total_s:.1f} s, single-threaded C"),
         "seconds": round(total_s, 2),
+        "cpu_model": cpu_model(),
+        "host_cores_available": len(os.sched_getaffinity(0)),
         "per_kernel_s": {name: round(sum(t[2] for t in timings if t[0] == name), 3)
                          for name in dict.fromkeys(t[0] for t in timings)},
     }
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def block_sweep(torch, z, K: int = 10) -> dict:
