@@ -34,6 +34,8 @@ the same work as one step (the reorder and the quantize as two oracle steps),
 twice.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --configs       (one JSON line: kernel times at the 4096x4096,
+       8 x 16M (2x4) and 64-shard shapes)
        python bench.py --block-sweep   (one JSON line: quantize / dequantize time
        and quantization error for every block size 32..4096, 8- and 4-bit codes,
        on the GQA weight, beside one global scale for the whole tensor)
@@ -340,6 +342,105 @@ def cpu_baseline(step: "Step", frac: float = 1.0, passes: int = 2):
     }
 
 
+def configs_bench(torch, z, K: int = 50) -> dict:
+    """Kernel times at the three smaller workload shapes (the 500M-element
+    bucket and the GQA layer are the step's rows). Each row is timed with HIP
+    events around K launches (the mean), after one untimed launch."""
+    import numpy as np
+
+    import synth
+
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream()
+
+    def to_dev(a):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        return t.view(torch.int16).view(torch.bfloat16).to(dev) if a.dtype == np.uint16 else t.to(dev)
+
+    def rows(table):
+        """table: [(name, fn, read bytes, write bytes)] -> {name: timing}"""
+        out = {}
+        for name, fn, rb, wb in table:
+            fn()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+            for a, b in ev:
+                a.record(stream)
+                fn()
+                b.record(stream)
+            torch.cuda.synchronize()
+            ms = sum(a.elapsed_time(b) for a, b in ev) / K
+            out[name] = {"ms": round(ms, 5), "in_GBps": round(rb / (ms * 1e-3) / 1e9, 1),
+                         "hbm_frac": round((rb + wb) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+            log(f"{name}: {ms * 1e3:.1f} us, {out[name]['hbm_frac']:.3f} of HBM peak")
+        return out
+
+    res = {}
+    # 4096 x 4096 weight, int8 block 256: quantize and dequantize
+    c1 = synth.QWZ_INT8_4096
+    n1, B1 = c1.numel, c1.block
+    x1 = to_dev(c1.weight())
+    q1c = torch.empty(n1, dtype=torch.uint8, device=dev)
+    q1s = torch.empty(n1 // B1, dtype=torch.float32, device=dev)
+    y1 = torch.empty_like(x1)
+    res[c1.name] = rows([
+        ("quantize_int8_b256", lambda: z.zpp_quantize_blocks(x1, z.ZPP_BF16, n1, B1, 8, q1c, q1s),
+         2 * n1, n1 + 4 * n1 // B1),
+        ("dequantize_int8_b256_bf16", lambda: z.zpp_dequantize_blocks(q1c, q1s, 8, n1, B1, y1, z.ZPP_BF16),
+         n1 + 4 * n1 // B1, 2 * n1),
+    ])
+    del x1, q1c, q1s, y1
+    # 8 ranks x 16M at 2 x 4, int4 block 128
+    c2 = synth.QGZ_INT4_2x4
+    n, g, N, B2 = c2.n_nodes, c2.gpus_per_node, c2.n_ranks, c2.block
+    P, S, C = c2.padded, c2.slice_len, c2.chunk_len
+    grads = to_dev(np.concatenate([c2.bucket(r) for r in range(N)]))
+    reord = torch.empty_like(grads)
+    q2c = torch.empty(N * P // 2, dtype=torch.uint8, device=dev)
+    q2s = torch.empty(N * P // B2, dtype=torch.float32, device=dev)
+    h2c = torch.empty(n * P // 2, dtype=torch.uint8, device=dev)
+    h2s = torch.empty(n * P // B2, dtype=torch.float32, device=dev)
+
+    def reorder_all():
+        for r in range(N):
+            z.zpp_reorder_slices(grads[r * P:], reord[r * P:], 2 * S, n, g)
+
+    reorder_all()
+    z.zpp_quantize_blocks(reord, z.ZPP_BF16, N * P, B2, 4, q2c, q2s)
+    torch.cuda.synchronize()
+    a, j = n - 1, g - 1  # rank 7's share: chunk j of node a's local ranks
+    one_off = a * g * P + j * C
+
+    def hop1_all():
+        for aa in range(n):
+            z.zpp_dequant_reduce_requant(q2c[aa * g * P // 2:], P // 2, q2s[aa * g * P // B2:], P // B2, g, 4, P, B2,
+                                         h2c[aa * P // 2:], h2s[aa * P // B2:], 4, None)
+
+    w1 = g * (C // 2 + 4 * C // B2)
+    res[c2.name] = rows([
+        ("reorder_bf16_8_ranks", reorder_all, 2 * N * P, 2 * N * P),
+        ("quantize_int4_b128_8_ranks", lambda: z.zpp_quantize_blocks(reord, z.ZPP_BF16, N * P, B2, 4, q2c, q2s),
+         2 * N * P, N * P // 2 + 4 * N * P // B2),
+        ("hop1_4way_one_share", lambda: z.zpp_dequant_reduce_requant(
+            q2c[one_off // 2:], P // 2, q2s[one_off // B2:], P // B2, g, 4, C, B2, h2c, h2s, 4, None),
+         w1, C // 2 + 4 * C // B2),
+        ("hop1_4way_all_8_shares", hop1_all, N * w1, N * (C // 2 + 4 * C // B2)),
+    ])
+    del grads, reord, q2c, q2s, h2c, h2s
+    # 64 int8 shards (block 2048) of a Llama-style layer, dequantized in one launch
+    c3 = synth.QWZ_DEQUANT_64
+    n3, B3 = c3.numel, c3.block
+    x3 = to_dev(c3.weight())
+    q3c = torch.empty(n3, dtype=torch.uint8, device=dev)
+    q3s = torch.empty(n3 // B3, dtype=torch.float32, device=dev)
+    z.zpp_quantize_blocks(x3, z.ZPP_BF16, n3, B3, 8, q3c, q3s)
+    y3 = torch.empty_like(x3)
+    res[c3.name] = rows([
+        ("dequantize_int8_b2048_64_shards", lambda: z.zpp_dequantize_blocks(q3c, q3s, 8, n3, B3, y3, z.ZPP_BF16),
+         n3 + 4 * n3 // B3, 2 * n3),
+    ])
+    return res
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -432,6 +533,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--block-sweep", action="store_true",
                     help="instead of the step: time and error of every block size on the GQA weight")
+    ap.add_argument("--configs", action="store_true",
+                    help="instead of the step: kernel times at the three smaller workload shapes")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -452,6 +555,9 @@ def main() -> int:
 
     if args.block_sweep:
         print(json.dumps({"block_sweep": block_sweep(torch, z)}), flush=True)
+        return 0
+    if args.configs:
+        print(json.dumps({"configs": configs_bench(torch, z)}), flush=True)
         return 0
 
     # plain copy of known size, for scaling the rocprofv3 byte counters

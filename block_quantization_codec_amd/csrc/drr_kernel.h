@@ -73,7 +73,7 @@ namespace {
 // Below this many waves at 32 elements per lane, lanes take 8 elements each
 // so that small outputs still spread over every SIMD.
 #ifndef ZPP_DRR_NARROW_WAVES
-#define ZPP_DRR_NARROW_WAVES 8192
+#define ZPP_DRR_NARROW_WAVES 4096
 #endif
 
 template <int BITS_IN_, int BITS_OUT, int LOG2B_, int E_>
@@ -255,11 +255,12 @@ __global__ __launch_bounds__(kBlockThreads) void drr_kernel(const uint8_t *__res
 
         float acc[U][E];
         // Inputs are consumed in batches whose loads are all issued before
-        // the batch is summed: full batches of RB, then of 8, then single
-        // inputs; whichever batch comes first starts the sums.
+        // the batch is summed: full batches of RB, then of 8, then of 4, then
+        // single inputs; whichever batch comes first starts the sums.
         int r = 0;
         consume<G, G::RB>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, e, r, acc);
         if constexpr (G::RB > 8) consume<G, 8>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, e, r, acc);
+        consume<G, 4>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, e, r, acc);
         consume<G, 1>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, e, r, acc);
 
         if (AVG || sum_out != nullptr) {

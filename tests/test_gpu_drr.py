@@ -174,7 +174,7 @@ def test_empty_is_a_no_op():
 
 @pytest.mark.parametrize("bits_in,bits_out,R", [(4, 4, 8), (8, 8, 3), (4, 0, 5)])
 def test_wide_lane_path(bits_in, bits_out, R):
-    """Outputs large enough for the 32-elements-per-lane layout (at least 8192 waves of
+    """Outputs large enough for the 32-elements-per-lane layout (at least 4096 waves of
     2048 elements), with a ragged tail; the small cases above use 8 elements per lane."""
     block = 256
     numel = 8192 * 2048 + 3 * 2048 + 5 * block
