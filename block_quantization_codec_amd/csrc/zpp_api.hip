@@ -130,8 +130,13 @@ zpp_status check_all(const Range (&rs)[N]) {
     return ZPP_OK;
 }
 
-zpp_status launched(hipError_t e) {
-    if (e != hipSuccess) {
+// A triple-chevron launch reports failure only through the thread's pending
+// HIP error. Clear whatever an earlier, unrelated call left there first, so
+// that a good launch is never reported as failed because of it.
+template <class Launch>
+zpp_status launch_checked(Launch &&launch) {
+    (void)hipGetLastError();
+    if (launch() != hipSuccess) {
         (void)hipGetLastError();
         return ZPP_ERR_LAUNCH;
     }
@@ -157,8 +162,10 @@ zpp_status zpp_quantize_blocks(const void *x, zpp_dtype x_dtype, int64_t numel, 
     if (overlap(oc, in) || overlap(os, in) || overlap(oc, os)) return ZPP_ERR_OVERLAP;
     const Range all[] = {in, oc, os};
     if (zpp_status s = check_all(all); s != ZPP_OK) return s;
-    return launched(zpp::launch_quantize(x, x_dtype == ZPP_FP32, numel, log2_of(block), bits, codes, scales,
-                                         static_cast<hipStream_t>(stream)));
+    return launch_checked([&] {
+        return zpp::launch_quantize(x, x_dtype == ZPP_FP32, numel, log2_of(block), bits, codes, scales,
+                   static_cast<hipStream_t>(stream));
+    });
 }
 
 zpp_status zpp_quantize_reordered(const void *x, zpp_dtype x_dtype, int64_t slice_elems, int32_t n_nodes,
@@ -181,9 +188,10 @@ zpp_status zpp_quantize_reordered(const void *x, zpp_dtype x_dtype, int64_t slic
     if (overlap(oc, in) || overlap(os, in) || overlap(oc, os)) return ZPP_ERR_OVERLAP;
     const Range all[] = {in, oc, os};
     if (zpp_status s = check_all(all); s != ZPP_OK) return s;
-    return launched(zpp::launch_quantize_reordered(x, x_dtype == ZPP_FP32, slice_elems, n_nodes, gpus_per_node,
-                                                   first_slice, n_slices, log2_of(block), bits, codes, scales,
-                                                   static_cast<hipStream_t>(stream)));
+    return launch_checked([&] {
+        return zpp::launch_quantize_reordered(x, x_dtype == ZPP_FP32, slice_elems, n_nodes, gpus_per_node,
+                   first_slice, n_slices, log2_of(block), bits, codes, scales, static_cast<hipStream_t>(stream));
+    });
 }
 
 zpp_status zpp_dequantize_blocks(const void *codes, const float *scales, int32_t bits, int64_t numel, int32_t block,
@@ -199,8 +207,10 @@ zpp_status zpp_dequantize_blocks(const void *codes, const float *scales, int32_t
     if (overlap(oy, ic) || overlap(oy, is)) return ZPP_ERR_OVERLAP;
     const Range all[] = {ic, is, oy};
     if (zpp_status s = check_all(all); s != ZPP_OK) return s;
-    return launched(zpp::launch_dequantize(codes, scales, bits, numel, log2_of(block), y, y_dtype == ZPP_FP32,
-                                           static_cast<hipStream_t>(stream)));
+    return launch_checked([&] {
+        return zpp::launch_dequantize(codes, scales, bits, numel, log2_of(block), y, y_dtype == ZPP_FP32,
+                   static_cast<hipStream_t>(stream));
+    });
 }
 
 zpp_status zpp_reorder_slices(const void *in, void *out, int64_t slice_bytes, int32_t n_nodes,
@@ -215,8 +225,9 @@ zpp_status zpp_reorder_slices(const void *in, void *out, int64_t slice_bytes, in
     if (overlap(ri, ro)) return ZPP_ERR_OVERLAP;
     const Range all[] = {ri, ro};
     if (zpp_status s = check_all(all); s != ZPP_OK) return s;
-    return launched(zpp::launch_reorder(in, out, slice_bytes, n_nodes, gpus_per_node,
-                                        static_cast<hipStream_t>(stream)));
+    return launch_checked([&] {
+        return zpp::launch_reorder(in, out, slice_bytes, n_nodes, gpus_per_node, static_cast<hipStream_t>(stream));
+    });
 }
 
 zpp_status zpp_dequant_reduce_requant(const void *codes_in, int64_t codes_stride_bytes, const float *scales_in,
@@ -249,9 +260,10 @@ zpp_status zpp_dequant_reduce_requant(const void *codes_in, int64_t codes_stride
     if (overlap(oc, os) || overlap(oc, ou) || overlap(os, ou)) return ZPP_ERR_OVERLAP;
     const Range all[] = {ic, is, oc, os, ou};
     if (zpp_status s = check_all(all); s != ZPP_OK) return s;
-    return launched(zpp::launch_drr(codes_in, codes_stride_bytes, scales_in, scales_stride, n_inputs, bits_in, numel,
-                                    log2_of(block), codes_out, scales_out, bits_out, sum_out,
-                                    static_cast<hipStream_t>(stream)));
+    return launch_checked([&] {
+        return zpp::launch_drr(codes_in, codes_stride_bytes, scales_in, scales_stride, n_inputs, bits_in, numel,
+                   log2_of(block), codes_out, scales_out, bits_out, sum_out, static_cast<hipStream_t>(stream));
+    });
 }
 
 zpp_status zpp_dequant_reduce_average(const void *codes_in, int64_t codes_stride_bytes, const float *scales_in,
@@ -272,9 +284,10 @@ zpp_status zpp_dequant_reduce_average(const void *codes_in, int64_t codes_stride
     if (overlap(ou, ic) || overlap(ou, is)) return ZPP_ERR_OVERLAP;
     const Range all[] = {ic, is, ou};
     if (zpp_status s = check_all(all); s != ZPP_OK) return s;
-    return launched(zpp::launch_drr_average(codes_in, codes_stride_bytes, scales_in, scales_stride, n_inputs,
-                                            bits_in, numel, log2_of(block), divisor, avg_out,
-                                            static_cast<hipStream_t>(stream)));
+    return launch_checked([&] {
+        return zpp::launch_drr_average(codes_in, codes_stride_bytes, scales_in, scales_stride, n_inputs, bits_in,
+                   numel, log2_of(block), divisor, avg_out, static_cast<hipStream_t>(stream));
+    });
 }
 
 const char *zpp_status_string(zpp_status status) {

@@ -19,7 +19,11 @@
  *   null stream). The call validates all arguments on the host first; if any
  *   check fails it returns an error code, launches nothing and leaves every
  *   output untouched. Faults during execution surface at the caller's next
- *   synchronization of the stream, as with any HIP kernel.
+ *   synchronization of the stream, as with any HIP kernel. Right before
+ *   its launch a call reads and clears the calling thread's pending HIP
+ *   error (hipGetLastError), so an error left there by an earlier call does
+ *   not survive it; a rejected launch returns ZPP_ERR_LAUNCH and leaves no
+ *   error pending.
  * - The caller allocates and owns every buffer; the library allocates
  *   nothing, keeps no per-call state and may be called from several threads
  *   and streams at once. Outputs must not overlap inputs or each other

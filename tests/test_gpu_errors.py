@@ -6,13 +6,15 @@ host memory passed as a device pointer (ZPP_ERR_POINTER), a buffer whose
 byte range runs past its allocation (ZPP_ERR_ARG), misaligned pointers
 (ZPP_ERR_ALIGN) and overlapping buffers (ZPP_ERR_OVERLAP). Pinned host
 memory, which the GPU can address, is accepted as input and gives the same
-result as device memory.
+result as device memory. A HIP error left pending by an unrelated earlier
+call does not make a good call fail.
 """
 from __future__ import annotations
 
 import numpy as np
 import pytest
 
+import oracle
 import synth
 from gpu_util import GUARD, Guarded, assert_bits_equal, dev, host, need_gpu, torch
 
@@ -104,3 +106,28 @@ def test_pinned_host_input_is_accepted():
     torch.cuda.synchronize()
     assert_bits_equal(host(c1), host(c2), "codes from pinned host input")
     assert_bits_equal(host(s1), host(s2), "scales from pinned host input")
+
+
+def test_pending_hip_error_does_not_fail_a_good_call():
+    """An error an earlier, unrelated HIP call left pending in this thread
+    (here: an attribute query for a device that does not exist) must not make
+    a valid launch report ZPP_ERR_LAUNCH; the call clears it. The runtime is
+    opened by the soname the library links, so it is the one already loaded."""
+    import ctypes
+    z = _z()
+    n, B = 4096, 256
+    x = synth.small_bf16(n, (0, 505), 0.02)
+    xd = dev(x)
+    c = torch.empty(n, dtype=torch.uint8, device="cuda")
+    s = torch.empty(n // B, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    value = ctypes.c_int(0)
+    assert hip.hipDeviceGetAttribute(ctypes.byref(value), 0, 100000) != 0   # no device 100000
+    assert hip.hipPeekAtLastError() != 0
+    z.zpp_quantize_blocks(xd, z.ZPP_BF16, n, B, 8, c, s)   # raises ZppError if it reports a failure
+    assert hip.hipPeekAtLastError() == 0
+    torch.cuda.synchronize()
+    oc, os_ = oracle.quantize(x, B, 8)
+    assert_bits_equal(host(c), oc, "codes after a pending error")
+    assert_bits_equal(host(s), os_, "scales after a pending error")
