@@ -70,8 +70,12 @@ namespace {
 #ifndef ZPP_DRR_NARROW_BATCH
 #define ZPP_DRR_NARROW_BATCH 16
 #endif
-// Below this many waves at 32 elements per lane, lanes take 8 elements each
-// so that small outputs still spread over every SIMD.
+// Elements per lane of the wide layout (16 or 32).
+#ifndef ZPP_DRR_WIDE_E
+#define ZPP_DRR_WIDE_E 32
+#endif
+// Below this many waves of the wide layout, lanes take 8 elements each so
+// that small outputs still spread over every SIMD.
 #ifndef ZPP_DRR_NARROW_WAVES
 #define ZPP_DRR_NARROW_WAVES 4096
 #endif
@@ -123,22 +127,33 @@ __device__ __forceinline__ void store_dwords(uint8_t *p, const uint32_t (&d)[ND]
 }
 
 // The codes of dword `w` of one input as binary32 products code * s, element
-// 0 first. FAST (4-bit codes only): a nibble moved to the top of a byte reads
-// as the signed byte 16 * code, and (16 * code) * (s / 16) is the same real
-// product as code * s, so it rounds identically whenever s / 16 is exact
-// (s == 0 or s >= 2^-122). 8-bit codes convert directly.
+// 0 first. FAST (4-bit codes only): flipping the top bit of a two's-complement
+// nibble q gives the unsigned nibble q + 8, and a byte converts to binary32
+// in one instruction (v_cvt_f32_ubyte0..3): the even nibbles masked in place
+// give q + 8, the odd ones 16 (q + 8). A fused multiply-add with s (or s / 16)
+// and -8 s then forms (q + 8) s - 8 s = q s exactly and rounds it once, which
+// is the correctly rounded product, whenever s / 16 is exact and -8 s finite:
+// s == 0 or 2^-122 <= |s| <= 2^124. An exact zero comes out as +0 where the
+// product may be -0, which no sum can tell apart: every sum starts from +0.
+// (Converting two nibbles per instruction as FP8 E4M3 bytes, exact for byte
+// values below 16, issues fewer instructions but measured slower on gfx950.)
+// 8-bit codes convert directly.
 template <int BITS_IN, bool FAST>
-__device__ __forceinline__ void dequant_dword(uint32_t w, float s, float s16, float (&p)[32 / BITS_IN]) {
+__device__ __forceinline__ void dequant_dword(uint32_t w, float s, float s16, float m8s, float (&p)[32 / BITS_IN]) {
     if constexpr (BITS_IN == 8) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) p[i] = static_cast<float>(static_cast<int8_t>(w >> (8 * i))) * s;
     } else if constexpr (FAST) {
-        const uint32_t even = (w << 4) & 0xF0F0F0F0u;  // byte i: code 2i << 4
-        const uint32_t odd = w & 0xF0F0F0F0u;          // byte i: code 2i+1 << 4
+        uint32_t even = (w ^ 0x88888888u) & 0x0F0F0F0Fu;  // byte i: q_2i + 8
+        uint32_t odd = (w ^ 0x88888888u) & 0xF0F0F0F0u;   // byte i: 16 (q_2i+1 + 8)
+        // Opaque to the optimizer, so that each byte converts straight from
+        // its dword instead of being extracted first.
+        asm("" : "+v"(even));
+        asm("" : "+v"(odd));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            p[2 * i] = static_cast<float>(static_cast<int8_t>(even >> (8 * i))) * s16;
-            p[2 * i + 1] = static_cast<float>(static_cast<int8_t>(odd >> (8 * i))) * s16;
+            p[2 * i] = __builtin_fmaf(static_cast<float>((even >> (8 * i)) & 0xFFu), s, m8s);
+            p[2 * i + 1] = __builtin_fmaf(static_cast<float>((odd >> (8 * i)) & 0xFFu), s16, m8s);
         }
     } else {
 #pragma unroll
@@ -156,11 +171,11 @@ __device__ __forceinline__ void accumulate(const uint32_t (&w)[NB][G::U][G::ND],
 #pragma unroll
         for (int u = 0; u < G::U; ++u) {
             const float sk = s[k][u];
-            const float s16 = sk * 0.0625f;
+            const float s16 = sk * 0.0625f, m8s = sk * -8.0f;
 #pragma unroll
             for (int d = 0; d < G::ND; ++d) {
                 float p[CPW];
-                dequant_dword<G::BITS_IN, FAST>(w[k][u][d], sk, s16, p);
+                dequant_dword<G::BITS_IN, FAST>(w[k][u][d], sk, s16, m8s, p);
 #pragma unroll
                 for (int i = 0; i < CPW; ++i) {
                     if (FIRST && k == 0)
@@ -204,7 +219,10 @@ __device__ __forceinline__ void sum_batch(const uint8_t *__restrict__ codes_in, 
 #pragma unroll
         for (int k = 0; k < NB; ++k)
 #pragma unroll
-            for (int u = 0; u < U; ++u) fast &= (s[k][u] == 0.0f) | (s[k][u] >= 0x1p-122f);  // s/16 exact
+            for (int u = 0; u < U; ++u) {  // s / 16 exact and -8 s finite
+                const float a = __builtin_fabsf(s[k][u]);
+                fast &= (a == 0.0f) | ((a >= 0x1p-122f) & (a <= 0x1p124f));
+            }
         if (fast)
             accumulate<G, NB, FIRST, true>(w, s, acc);
         else
@@ -323,9 +341,9 @@ hipError_t launch_e(const DrrArgs &a) {
 
 template <int BITS_IN, int BITS_OUT, int LOG2B, bool AVG>
 hipError_t launch(const DrrArgs &a) {
-    using Wide = DrrGeom<BITS_IN, BITS_OUT, LOG2B, 32>;
+    using Wide = DrrGeom<BITS_IN, BITS_OUT, LOG2B, ZPP_DRR_WIDE_E>;
     const int64_t wide_waves = (a.numel + Wide::TILE - 1) / Wide::TILE;
-    if (wide_waves >= ZPP_DRR_NARROW_WAVES) return launch_e<BITS_IN, BITS_OUT, LOG2B, 32, AVG>(a);
+    if (wide_waves >= ZPP_DRR_NARROW_WAVES) return launch_e<BITS_IN, BITS_OUT, LOG2B, ZPP_DRR_WIDE_E, AVG>(a);
     return launch_e<BITS_IN, BITS_OUT, LOG2B, 8, AVG>(a);
 }
 
