@@ -15,17 +15,18 @@
 // of contributing GPUs (one correctly rounded binary32 division): page
 // "ZeRO Stage 2: Gradient Partitioning", step 2 of the stage-2 flow, where
 // the reduce-scatter hands each GPU the average of its shard. Any code bytes
-// and scales are accepted: 4-bit products use the s / 16 shortcut only where
-// it is exact, and the first sum, written acc = p, is made exact by adding +0
-// to every finished sum (see sum_batch).
+// and scales are accepted: 4-bit products use a fused multiply-add shortcut
+// only where it is exact, and the first sum, written acc = p, is made exact by
+// adding +0 to every finished sum (see add_batch).
 //
 // Layout of the work: a lane owns E consecutive elements of a wave segment of
 // 64 E elements: E = 32 (one 16-byte vector of 4-bit codes per input, so
 // each load instruction reads one contiguous kilobyte of an input), or E = 8
 // for small outputs, which then still spread over every SIMD. Inputs are
 // read a batch at a time, all loads of a batch in flight before the batch is
-// summed in input order. The requantized block maximum is reduced across the
-// block's lanes with DPP / permlane swaps.
+// summed in input order; with E = 8 the next batch's loads are also issued
+// before the current batch is summed. The requantized block maximum is
+// reduced across the block's lanes with DPP / permlane swaps.
 #pragma once
 
 #include "zpp_device.h"
@@ -66,9 +67,14 @@ namespace {
 #define ZPP_DRR_BATCH 8
 #endif
 // Inputs per load batch of the narrow layout (one code dword and one scale
-// per input and lane; a wave can keep at most 63 loads in flight).
+// per input and lane; with the next batch in flight as well, 4 * 8 = 32
+// loads, within the 63 a wave can keep outstanding).
 #ifndef ZPP_DRR_NARROW_BATCH
-#define ZPP_DRR_NARROW_BATCH 16
+#define ZPP_DRR_NARROW_BATCH 8
+#endif
+// 1: the narrow layout loads each batch while it sums the previous one.
+#ifndef ZPP_DRR_NARROW_OVERLAP
+#define ZPP_DRR_NARROW_OVERLAP 1
 #endif
 // Elements per lane of the wide layout (16 or 32).
 #ifndef ZPP_DRR_WIDE_E
@@ -94,6 +100,7 @@ struct DrrGeom {
     static constexpr int ND = E * BITS_IN / 32;            // code dwords per lane per input
     static constexpr int QMAX = BITS_OUT == 8 ? 127 : 7;
     static constexpr int RB = E == 8 ? ZPP_DRR_NARROW_BATCH : ZPP_DRR_BATCH;  // inputs per load batch
+    static constexpr bool OVERLAP = E == 8 && ZPP_DRR_NARROW_OVERLAP;           // see consume_overlapped
 };
 
 template <int ND>
@@ -188,45 +195,75 @@ __device__ __forceinline__ void accumulate(const uint32_t (&w)[NB][G::U][G::ND],
     }
 }
 
-// Add inputs r0 .. r0+NB-1 (in that order) into acc. FIRST: input r0 starts
-// the sums, written acc = p instead of acc = +0 + p. The two differ only when
-// p is -0 (a negative code times a zero scale, or a zero code times a
-// negative one), and then only as long as every later product is -0 as well:
-// -0 + x == +0 + x for every other x. The kernel adds +0 to each finished sum
-// before writing it (a sum that starts at +0 is never -0), and a requantized
-// sum gets the same codes and scale either way.
-template <typename G, int NB, bool FIRST>
-__device__ __forceinline__ void sum_batch(const uint8_t *__restrict__ codes_in, int64_t codes_stride,
-                                          const float *__restrict__ scales_in, int64_t scales_stride, int r0,
-                                          const int64_t (&e)[G::U], float (&acc)[G::U][G::E]) {
-    constexpr int U = G::U, BITS_IN = G::BITS_IN;
-    uint32_t w[NB][U][G::ND];
-    float s[NB][U];
+// The codes and scales of NB consecutive inputs, as one lane loads them.
+template <typename G, int NB>
+struct Batch {
+    uint32_t w[NB][G::U][G::ND];
+    float s[NB][G::U];
+};
+
+// A lane's byte offsets within one input: of its code vectors and of their
+// block scales. Input r's data then sits at a wave-uniform base (held in
+// scalar registers) plus these offsets, the same for every input, so a load
+// needs no per-input vector address. A launch covers fewer than 2^29
+// elements, so every offset fits in 32 bits.
+template <typename G>
+struct LaneOffsets {
+    uint32_t code[G::U];
+    uint32_t scale[G::U];
+};
+
+template <typename G, int NB>
+__device__ __forceinline__ void load_batch(const uint8_t *__restrict__ codes_in, int64_t codes_stride,
+                                           const float *__restrict__ scales_in, int64_t scales_stride, int r0,
+                                           const LaneOffsets<G> &o, Batch<G, NB> &b) {
+    // Scales first: the batch's choice of product formula needs all of them,
+    // while each input's codes are needed only when that input is summed.
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+        const uint8_t *sc = reinterpret_cast<const uint8_t *>(scales_in + static_cast<int64_t>(r0 + k) * scales_stride);
+#pragma unroll
+        for (int u = 0; u < G::U; ++u) b.s[k][u] = *reinterpret_cast<const float *>(sc + o.scale[u]);
+    }
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
         const uint8_t *c = codes_in + static_cast<int64_t>(r0 + k) * codes_stride;
-        const float *sc = scales_in + static_cast<int64_t>(r0 + k) * scales_stride;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            load_dwords<G::ND>(c + e[u] * BITS_IN / 8, w[k][u]);
-            s[k][u] = sc[e[u] >> G::LOG2B];
-        }
+        for (int u = 0; u < G::U; ++u) load_dwords<G::ND>(c + o.code[u], b.w[k][u]);
     }
-    if constexpr (BITS_IN == 8) {
-        accumulate<G, NB, FIRST, true>(w, s, acc);
+    // Every load of the batch is issued before anything that uses one.
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Add a loaded batch into acc, in input order. FIRST: the batch's first input
+// starts the sums, written acc = p instead of acc = +0 + p. The two differ
+// only when p is -0 (a negative code times a zero scale, or a zero code times
+// a negative one), and then only as long as every later product is -0 as
+// well: -0 + x == +0 + x for every other x. The kernel adds +0 to each
+// finished sum before writing it (a sum that starts at +0 is never -0), and a
+// requantized sum gets the same codes and scale either way.
+template <typename G, int NB, bool FIRST>
+__device__ __forceinline__ void add_batch(const Batch<G, NB> &b, float (&acc)[G::U][G::E]) {
+    if constexpr (G::BITS_IN == 8) {
+        accumulate<G, NB, FIRST, true>(b.w, b.s, acc);
     } else {
-        bool fast = true;
+        // Every |s| of the batch as its bit pattern without the sign, shifted
+        // left by one (t), which orders like |s| with infinities and NaNs
+        // above every finite value: the largest t, and the smallest t - 1,
+        // where a zero scale wraps to the top and so never counts.
+        uint32_t hi = 0u, lo = ~0u;
 #pragma unroll
         for (int k = 0; k < NB; ++k)
 #pragma unroll
-            for (int u = 0; u < U; ++u) {  // s / 16 exact and -8 s finite
-                const float a = __builtin_fabsf(s[k][u]);
-                fast &= (a == 0.0f) | ((a >= 0x1p-122f) & (a <= 0x1p124f));
+            for (int u = 0; u < G::U; ++u) {
+                const uint32_t t = as_u(b.s[k][u]) << 1;
+                hi = max(hi, t);
+                lo = min(lo, t - 1u);
             }
-        if (fast)
-            accumulate<G, NB, FIRST, true>(w, s, acc);
+        if ((hi <= (as_u(0x1p124f) << 1)) & (lo >= (as_u(0x1p-122f) << 1) - 1u))  // s/16 exact, -8 s finite
+            accumulate<G, NB, FIRST, true>(b.w, b.s, acc);
         else
-            accumulate<G, NB, FIRST, false>(w, s, acc);
+            accumulate<G, NB, FIRST, false>(b.w, b.s, acc);
     }
 }
 
@@ -235,21 +272,63 @@ __device__ __forceinline__ void sum_batch(const uint8_t *__restrict__ codes_in, 
 template <typename G, int NB>
 __device__ __forceinline__ void consume(const uint8_t *__restrict__ codes_in, int64_t codes_stride,
                                         const float *__restrict__ scales_in, int64_t scales_stride, int n_inputs,
-                                        const int64_t (&e)[G::U], int &r, float (&acc)[G::U][G::E]) {
+                                        const LaneOffsets<G> &o, int &r, float (&acc)[G::U][G::E]) {
     if (r == 0) {
         if (NB > n_inputs) return;
-        sum_batch<G, NB, true>(codes_in, codes_stride, scales_in, scales_stride, 0, e, acc);
+        Batch<G, NB> b;
+        load_batch<G, NB>(codes_in, codes_stride, scales_in, scales_stride, 0, o, b);
+        add_batch<G, NB, true>(b, acc);
         r = NB;
     }
-    for (; r + NB <= n_inputs; r += NB)
-        sum_batch<G, NB, false>(codes_in, codes_stride, scales_in, scales_stride, r, e, acc);
+    for (; r + NB <= n_inputs; r += NB) {
+        Batch<G, NB> b;
+        load_batch<G, NB>(codes_in, codes_stride, scales_in, scales_stride, r, o, b);
+        add_batch<G, NB, false>(b, acc);
+    }
 }
+
+// As consume, with each batch's loads issued before the previous batch is
+// summed, so that a wave's loads overlap its own arithmetic (two batches of
+// registers, used in turn). Every sum of a batch follows the loads of the
+// next batch without a branch in between, so the sum waits for its own
+// batch's loads only. The sums must already hold +0 (no FIRST batch).
+template <typename G, int NB>
+__device__ __forceinline__ void consume_overlapped(const uint8_t *__restrict__ codes_in, int64_t codes_stride,
+                                                   const float *__restrict__ scales_in, int64_t scales_stride,
+                                                   int n_inputs, const LaneOffsets<G> &o, int &r,
+                                                   float (&acc)[G::U][G::E]) {
+    if (r + NB > n_inputs) return;
+    Batch<G, NB> a, b;
+    load_batch<G, NB>(codes_in, codes_stride, scales_in, scales_stride, r, o, a);
+    for (;;) {
+        if (r + 2 * NB > n_inputs) {
+            add_batch<G, NB, false>(a, acc);
+            r += NB;
+            return;
+        }
+        load_batch<G, NB>(codes_in, codes_stride, scales_in, scales_stride, r + NB, o, b);
+        add_batch<G, NB, false>(a, acc);
+        r += NB;
+        if (r + 2 * NB > n_inputs) {
+            add_batch<G, NB, false>(b, acc);
+            r += NB;
+            return;
+        }
+        load_batch<G, NB>(codes_in, codes_stride, scales_in, scales_stride, r + NB, o, a);
+        add_batch<G, NB, false>(b, acc);
+        r += NB;
+    }
+}
+
+// Elements one launch covers at most; a multiple of every block size and
+// tile, small enough that every lane offset fits in 32 bits.
+constexpr int64_t kDrrChunk = INT64_C(1) << 29;
 
 template <int BITS_IN, int BITS_OUT, int LOG2B, int E, bool AVG>
 __global__ __launch_bounds__(kBlockThreads) void drr_kernel(const uint8_t *__restrict__ codes_in,
                                                             int64_t codes_stride,
                                                             const float *__restrict__ scales_in,
-                                                            int64_t scales_stride, int n_inputs, int64_t numel,
+                                                            int64_t scales_stride, int n_inputs, int numel,
                                                             uint8_t *__restrict__ codes_out,
                                                             float *__restrict__ scales_out,
                                                             float *__restrict__ sum_out, float divisor) {
@@ -258,35 +337,50 @@ __global__ __launch_bounds__(kBlockThreads) void drr_kernel(const uint8_t *__res
     constexpr int U = G::U;
 
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t wave = xcd_block(blockIdx.x, gridDim.x) * (kBlockThreads / kWave) + (threadIdx.x / kWave);
-    const int64_t n_waves = static_cast<int64_t>(gridDim.x) * (kBlockThreads / kWave);
+    const int wave = static_cast<int>(xcd_block(blockIdx.x, gridDim.x)) * (kBlockThreads / kWave) +
+                     static_cast<int>(threadIdx.x / kWave);
+    const int n_waves = static_cast<int>(gridDim.x) * (kBlockThreads / kWave);
 
-    for (int64_t t0 = wave * G::TILE; t0 < numel; t0 += n_waves * G::TILE) {
-        int64_t e[U];
+    for (int64_t t0 = static_cast<int64_t>(wave) * G::TILE; t0 < numel;
+         t0 += static_cast<int64_t>(n_waves) * G::TILE) {
+        uint32_t e[U];
         bool ok[U];
+        LaneOffsets<G> o;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t e0 = t0 + static_cast<int64_t>(u) * G::SEG + lane * E;
             ok[u] = e0 < numel;
-            e[u] = ok[u] ? e0 : 0;
+            e[u] = ok[u] ? static_cast<uint32_t>(e0) : 0u;
+            o.code[u] = e[u] * BITS_IN / 8;
+            o.scale[u] = (e[u] >> LOG2B) * 4u;
         }
 
         float acc[U][E];
         // Inputs are consumed in batches whose loads are all issued before
         // the batch is summed: full batches of RB, then of 8, then of 4, then
-        // single inputs; whichever batch comes first starts the sums.
+        // single inputs; whichever batch comes first starts the sums. The
+        // narrow layout, whose waves are few, also overlaps each batch's
+        // loads with the previous batch's sums; its sums start from +0.
         int r = 0;
-        consume<G, G::RB>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, e, r, acc);
-        if constexpr (G::RB > 8) consume<G, 8>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, e, r, acc);
-        consume<G, 4>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, e, r, acc);
-        consume<G, 1>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, e, r, acc);
+        if constexpr (G::OVERLAP) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int i = 0; i < E; ++i) acc[u][i] = 0.0f;
+            consume_overlapped<G, G::RB>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, o, r, acc);
+        } else {
+            consume<G, G::RB>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, o, r, acc);
+        }
+        if constexpr (G::RB > 8) consume<G, 8>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, o, r, acc);
+        consume<G, 4>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, o, r, acc);
+        consume<G, 1>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, o, r, acc);
 
         if (AVG || sum_out != nullptr) {
 #pragma unroll
             for (int u = 0; u < U; ++u)
 #pragma unroll
                 for (int i = 0; i < E; ++i) {
-                    float v = acc[u][i] + 0.0f;      // -0 -> +0 (see sum_batch), any other value unchanged
+                    float v = acc[u][i] + 0.0f;      // -0 -> +0 (see add_batch), any other value unchanged
                     if constexpr (AVG) v = v / divisor;  // IEEE division
                     acc[u][i] = v;
                 }
@@ -295,7 +389,7 @@ __global__ __launch_bounds__(kBlockThreads) void drr_kernel(const uint8_t *__res
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 if (!ok[u]) continue;
-                float *dst = sum_out + e[u];
+                float *dst = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(sum_out) + e[u] * 4u);
 #pragma unroll
                 for (int v = 0; v < E / 4; ++v)
                     st_out<u32x4>(dst + 4 * v, u32x4{as_u(acc[u][4 * v]), as_u(acc[u][4 * v + 1]),
@@ -323,20 +417,30 @@ __global__ __launch_bounds__(kBlockThreads) void drr_kernel(const uint8_t *__res
                 pack_codes<E, BITS_OUT>(mg, cw);
                 if (!ok[u]) continue;
                 store_dwords<E * BITS_OUT / 32>(codes_out + e[u] * BITS_OUT / 8, cw);
-                if (u == 0 && (lane & (G::L - 1)) == 0) scales_out[e[u] >> LOG2B] = sc;
+                if (u == 0 && (lane & (G::L - 1)) == 0)
+                    *reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(scales_out) + o.scale[0]) = sc;
             }
         }
     }
 }
 
+// One launch per chunk of at most kDrrChunk elements (blocks are independent).
 template <int BITS_IN, int BITS_OUT, int LOG2B, int E, bool AVG>
 hipError_t launch_e(const DrrArgs &a) {
     using G = DrrGeom<BITS_IN, BITS_OUT, LOG2B, E>;
-    const int64_t tiles = (a.numel + G::TILE - 1) / G::TILE;
-    drr_kernel<BITS_IN, BITS_OUT, LOG2B, E, AVG><<<stream_grid(tiles), kBlockThreads, 0, a.stream>>>(
-        static_cast<const uint8_t *>(a.codes_in), a.cstride, a.scales_in, a.sstride, a.n_inputs, a.numel,
-        static_cast<uint8_t *>(a.codes_out), a.scales_out, a.sum_out, a.divisor);
-    return hipGetLastError();
+    for (int64_t done = 0; done < a.numel; done += kDrrChunk) {
+        const int64_t n = a.numel - done < kDrrChunk ? a.numel - done : kDrrChunk;
+        const int64_t tiles = (n + G::TILE - 1) / G::TILE;
+        drr_kernel<BITS_IN, BITS_OUT, LOG2B, E, AVG><<<stream_grid(tiles), kBlockThreads, 0, a.stream>>>(
+            static_cast<const uint8_t *>(a.codes_in) + done * BITS_IN / 8, a.cstride, a.scales_in + (done >> LOG2B),
+            a.sstride, a.n_inputs, static_cast<int>(n),
+            a.codes_out ? static_cast<uint8_t *>(a.codes_out) + done * BITS_OUT / 8 : nullptr,
+            a.scales_out ? a.scales_out + (done >> LOG2B) : nullptr, a.sum_out ? a.sum_out + done : nullptr,
+            a.divisor);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
 }
 
 template <int BITS_IN, int BITS_OUT, int LOG2B, bool AVG>

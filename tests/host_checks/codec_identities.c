@@ -10,8 +10,14 @@
  *              taken with the given stride (stride 1: all of them).
  *   ties       the same quotient for x within 3 ulps of (k + 1/2) s, every k,
  *              random normal s >= 2^-96: q1 == x / s bit for bit.
+ *   nibble     the 4-bit products of the hop kernels: for every code q in
+ *              [-8, 7] and scale s of magnitude 0 or in [2^-122, 2^124],
+ *              fma(q + 8, s, -8 s) and fma(16 (q + 8), s / 16, -8 s) equal
+ *              RN(q * s) (bit for bit, except that an exact zero may differ
+ *              in sign), over every significand (taken with the given
+ *              stride) of binades spread over that range, both signs.
  *
- * Usage: codec_identities <scale|markstein|ties> <param>; exits 1 on any
+ * Usage: codec_identities <scale|markstein|ties|nibble> <param>; exits 1 on any
  * mismatch. This is host-side test code; it does not run on the GPU.
  */
 #include <math.h>
@@ -109,9 +115,41 @@ static long check_ties(long iters) {
     return bad;
 }
 
+static long nibble_one(float s) {
+    long bad = 0;
+    const float m8s = s * -8.0f, s16 = s * 0.0625f;
+    for (int q = -8; q <= 7; ++q) {
+        const float want = (float)q * s;
+        const float a = fmaf((float)(q + 8), s, m8s);
+        const float b = fmaf((float)(16 * (q + 8)), s16, m8s);
+        if (want == 0.0f) {
+            bad += (a != 0.0f) + (b != 0.0f);
+        } else {
+            bad += (u32(a) != u32(want)) + (u32(b) != u32(want));
+        }
+    }
+    return bad;
+}
+
+static long check_nibble(int stride) {
+    static const int binades[] = {-122, -121, -100, -64, -2, -1, 0, 1, 63, 100, 122, 123};
+    long bad = 0, n = 0;
+    for (unsigned i = 0; i < sizeof binades / sizeof binades[0]; ++i) {
+        const uint32_t e = (uint32_t)(127 + binades[i]) << 23;
+        for (uint32_t m = 0; m < (1u << 23); m += (uint32_t)stride) {
+            bad += nibble_one(f32(e | m)) + nibble_one(-f32(e | m));
+            n += 2;
+        }
+    }
+    const float ends[] = {0.0f, -0.0f, 0x1p124f, -0x1p124f, 0x1p-122f, -0x1p-122f};
+    for (unsigned i = 0; i < sizeof ends / sizeof ends[0]; ++i, ++n) bad += nibble_one(ends[i]);
+    printf("nibble: %ld scales x 16 codes x 2 forms, mismatches %ld\n", n, bad);
+    return bad;
+}
+
 int main(int argc, char **argv) {
     if (argc != 3) {
-        fprintf(stderr, "usage: %s <scale|markstein|ties> <param>\n", argv[0]);
+        fprintf(stderr, "usage: %s <scale|markstein|ties|nibble> <param>\n", argv[0]);
         return 2;
     }
     const long p = atol(argv[2]);
@@ -119,6 +157,7 @@ int main(int argc, char **argv) {
     if (!strcmp(argv[1], "scale")) bad = check_scale((int)p);
     else if (!strcmp(argv[1], "markstein")) bad = check_markstein((int)p);
     else if (!strcmp(argv[1], "ties")) bad = check_ties(p);
+    else if (!strcmp(argv[1], "nibble")) bad = check_nibble((int)p);
     else return 2;
     return bad ? 1 : 0;
 }

@@ -5,8 +5,9 @@ every entry point. The input is a seeded pattern of 2^22 values, scaled in
 each 2^22-element tile by its own power of two, so a 32-bit wrap of an index
 or byte offset would read or write visibly different data. Outputs are
 compared with the oracle on sampled blocks (the first and last blocks, the
-blocks around element 2^31, and random ones); blocks are independent, so the
-oracle recomputes exactly those from the same input values.
+blocks around element 2^31 and around every multiple of 2^29, where the hop
+reduction starts another launch, and random ones); blocks are independent, so
+the oracle recomputes exactly those from the same input values.
 """
 from __future__ import annotations
 
@@ -23,6 +24,7 @@ M = 1 << 22            # pattern length (elements)
 TILES = 517            # tiles of M elements
 N = TILES * M          # 2,168,455,168 > 2^31
 EDGE = 1 << 31         # first element whose bf16 byte offset needs 33 bits
+CHUNK = 1 << 29        # the hop kernels launch once per this many elements
 
 
 @pytest.fixture(scope="module")
@@ -43,8 +45,8 @@ def x():
 def _sample_blocks(block: int, seed: int) -> np.ndarray:
     nb = N // block
     rng = np.random.default_rng([seed, block])
-    edge = EDGE // block
-    idx = np.concatenate([np.arange(16), np.arange(nb - 16, nb), np.arange(edge - 16, edge + 16),
+    edges = [EDGE // block] + [k * CHUNK // block for k in range(1, N // CHUNK + 1)]
+    idx = np.concatenate([np.arange(16), np.arange(nb - 16, nb), *[np.arange(e - 16, e + 16) for e in edges],
                           rng.choice(nb, 2000, replace=False)])
     return np.unique(idx)
 

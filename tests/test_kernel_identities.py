@@ -3,8 +3,9 @@ slower operations (the kernels' results are separately compared with the
 oracle on the GPU). Quick sampled sweeps by default; set
 ZPP_EXHAUSTIVE_IDENTITIES=1 for the exhaustive ones (several minutes):
 every significand of five binades for the block-scale identity, every
-(x, absmax) pair of finite bfloat16 values for Markstein's division, and
-about 3.6e9 near-tie binary32 values.
+(x, absmax) pair of finite bfloat16 values for Markstein's division,
+about 3.6e9 near-tie binary32 values, and every significand of twelve
+binades for the 4-bit product shortcut.
 """
 from __future__ import annotations
 
@@ -42,3 +43,7 @@ def test_markstein_codes_on_bf16_domain(exe):
 
 def test_markstein_quotients_near_ties(exe):
     _run(exe, "ties", 2_000_000 if FULL else 3_000)
+
+
+def test_nibble_products_by_fused_multiply_add(exe):
+    _run(exe, "nibble", 1 if FULL else 997)
