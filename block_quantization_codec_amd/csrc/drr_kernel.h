@@ -134,20 +134,27 @@ __device__ __forceinline__ void store_dwords(uint8_t *p, const uint32_t (&d)[ND]
 }
 
 // The codes of dword `w` of one input as binary32 products code * s, element
-// 0 first. FAST (4-bit codes only): flipping the top bit of a two's-complement
-// nibble q gives the unsigned nibble q + 8, and a byte converts to binary32
-// in one instruction (v_cvt_f32_ubyte0..3): the even nibbles masked in place
-// give q + 8, the odd ones 16 (q + 8). A fused multiply-add with s (or s / 16)
-// and -8 s then forms (q + 8) s - 8 s = q s exactly and rounds it once, which
-// is the correctly rounded product, whenever s / 16 is exact and -8 s finite:
-// s == 0 or 2^-122 <= |s| <= 2^124. An exact zero comes out as +0 where the
+// 0 first. FAST: flipping the top bit of a two's-complement code q gives the
+// unsigned q + 2^(bits-1) (q + 8 for a nibble, q + 128 for a byte), and a
+// byte converts to binary32 in one instruction (v_cvt_f32_ubyte0..3; 4-bit
+// codes: the even nibbles masked in place give q + 8, the odd ones
+// 16 (q + 8)). A fused multiply-add with s (or s / 16) and mb = -2^(bits-1) s
+// then forms (q + 2^(bits-1)) s - 2^(bits-1) s = q s exactly and rounds it
+// once, which is the correctly rounded product whenever mb is finite and
+// s / 16 exact: s == 0 or 2^-122 <= |s| <= 2^124 for 4-bit codes, and
+// |s| <= 2^120 for 8-bit codes. An exact zero comes out as +0 where the
 // product may be -0, which no sum can tell apart: every sum starts from +0.
 // (Converting two nibbles per instruction as FP8 E4M3 bytes, exact for byte
-// values below 16, issues fewer instructions but measured slower on gfx950.)
-// 8-bit codes convert directly.
+// values below 16, issues fewer instructions but measured slower on gfx950,
+// as did the sign-extending SDWA conversion followed by a multiply.)
 template <int BITS_IN, bool FAST>
-__device__ __forceinline__ void dequant_dword(uint32_t w, float s, float s16, float m8s, float (&p)[32 / BITS_IN]) {
-    if constexpr (BITS_IN == 8) {
+__device__ __forceinline__ void dequant_dword(uint32_t w, float s, float s16, float mb, float (&p)[32 / BITS_IN]) {
+    if constexpr (BITS_IN == 8 && FAST) {
+        uint32_t u = w ^ 0x80808080u;  // byte i: q_i + 128
+        asm("" : "+v"(u));             // opaque: each byte converts straight from the dword
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = __builtin_fmaf(static_cast<float>((u >> (8 * i)) & 0xFFu), s, mb);
+    } else if constexpr (BITS_IN == 8) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) p[i] = static_cast<float>(static_cast<int8_t>(w >> (8 * i))) * s;
     } else if constexpr (FAST) {
@@ -159,8 +166,8 @@ __device__ __forceinline__ void dequant_dword(uint32_t w, float s, float s16, fl
         asm("" : "+v"(odd));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            p[2 * i] = __builtin_fmaf(static_cast<float>((even >> (8 * i)) & 0xFFu), s, m8s);
-            p[2 * i + 1] = __builtin_fmaf(static_cast<float>((odd >> (8 * i)) & 0xFFu), s16, m8s);
+            p[2 * i] = __builtin_fmaf(static_cast<float>((even >> (8 * i)) & 0xFFu), s, mb);
+            p[2 * i + 1] = __builtin_fmaf(static_cast<float>((odd >> (8 * i)) & 0xFFu), s16, mb);
         }
     } else {
 #pragma unroll
@@ -178,11 +185,11 @@ __device__ __forceinline__ void accumulate(const uint32_t (&w)[NB][G::U][G::ND],
 #pragma unroll
         for (int u = 0; u < G::U; ++u) {
             const float sk = s[k][u];
-            const float s16 = sk * 0.0625f, m8s = sk * -8.0f;
+            const float s16 = sk * 0.0625f, mb = sk * (G::BITS_IN == 8 ? -128.0f : -8.0f);
 #pragma unroll
             for (int d = 0; d < G::ND; ++d) {
                 float p[CPW];
-                dequant_dword<G::BITS_IN, FAST>(w[k][u][d], sk, s16, m8s, p);
+                dequant_dword<G::BITS_IN, FAST>(w[k][u][d], sk, s16, mb, p);
 #pragma unroll
                 for (int i = 0; i < CPW; ++i) {
                     if (FIRST && k == 0)
@@ -244,27 +251,28 @@ __device__ __forceinline__ void load_batch(const uint8_t *__restrict__ codes_in,
 // requantized sum gets the same codes and scale either way.
 template <typename G, int NB, bool FIRST>
 __device__ __forceinline__ void add_batch(const Batch<G, NB> &b, float (&acc)[G::U][G::E]) {
-    if constexpr (G::BITS_IN == 8) {
+    // Every |s| of the batch as its bit pattern without the sign, shifted
+    // left by one (t), which orders like |s| with infinities and NaNs above
+    // every finite value: the largest t, and the smallest t - 1, where a zero
+    // scale wraps to the top and so never counts.
+    uint32_t hi = 0u, lo = ~0u;
+#pragma unroll
+    for (int k = 0; k < NB; ++k)
+#pragma unroll
+        for (int u = 0; u < G::U; ++u) {
+            const uint32_t t = as_u(b.s[k][u]) << 1;
+            hi = max(hi, t);
+            if constexpr (G::BITS_IN == 4) lo = min(lo, t - 1u);
+        }
+    bool fast;
+    if constexpr (G::BITS_IN == 8)
+        fast = hi <= (as_u(0x1p120f) << 1);  // -128 s finite
+    else
+        fast = (hi <= (as_u(0x1p124f) << 1)) & (lo >= (as_u(0x1p-122f) << 1) - 1u);  // -8 s finite, s/16 exact
+    if (fast)
         accumulate<G, NB, FIRST, true>(b.w, b.s, acc);
-    } else {
-        // Every |s| of the batch as its bit pattern without the sign, shifted
-        // left by one (t), which orders like |s| with infinities and NaNs
-        // above every finite value: the largest t, and the smallest t - 1,
-        // where a zero scale wraps to the top and so never counts.
-        uint32_t hi = 0u, lo = ~0u;
-#pragma unroll
-        for (int k = 0; k < NB; ++k)
-#pragma unroll
-            for (int u = 0; u < G::U; ++u) {
-                const uint32_t t = as_u(b.s[k][u]) << 1;
-                hi = max(hi, t);
-                lo = min(lo, t - 1u);
-            }
-        if ((hi <= (as_u(0x1p124f) << 1)) & (lo >= (as_u(0x1p-122f) << 1) - 1u))  // s/16 exact, -8 s finite
-            accumulate<G, NB, FIRST, true>(b.w, b.s, acc);
-        else
-            accumulate<G, NB, FIRST, false>(b.w, b.s, acc);
-    }
+    else
+        accumulate<G, NB, FIRST, false>(b.w, b.s, acc);
 }
 
 // Sum every remaining full batch of NB inputs from input r on (r advances).

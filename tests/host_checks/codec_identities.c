@@ -16,8 +16,10 @@
  *              RN(q * s) (bit for bit, except that an exact zero may differ
  *              in sign), over every significand (taken with the given
  *              stride) of binades spread over that range, both signs.
+ *   byte       the same for 8-bit codes q in [-128, 127] and |s| <= 2^120:
+ *              fma(q + 128, s, -128 s) equals RN(q * s).
  *
- * Usage: codec_identities <scale|markstein|ties|nibble> <param>; exits 1 on any
+ * Usage: codec_identities <scale|markstein|ties|nibble|byte> <param>; exits 1 on any
  * mismatch. This is host-side test code; it does not run on the GPU.
  */
 #include <math.h>
@@ -147,9 +149,36 @@ static long check_nibble(int stride) {
     return bad;
 }
 
+static long byte_one(float s) {
+    long bad = 0;
+    const float mb = s * -128.0f;
+    for (int q = -128; q <= 127; ++q) {
+        const float want = (float)q * s, got = fmaf((float)(q + 128), s, mb);
+        bad += want == 0.0f ? got != 0.0f : u32(got) != u32(want);
+    }
+    return bad;
+}
+
+static long check_byte(int stride) {
+    static const int binades[] = {-145, -140, -127, -126, -122, -64, -1, 0, 1, 63, 118, 119};
+    long bad = 0, n = 0;
+    for (unsigned i = 0; i < sizeof binades / sizeof binades[0]; ++i) {
+        for (uint32_t m = 0; m < (1u << 23); m += (uint32_t)stride) {
+            /* binades below 2^-126 are subnormal: significand m scaled by 2^(b + 23 - 126) */
+            const float s = binades[i] < -126 ? f32(m >> (-126 - binades[i])) : f32(((uint32_t)(127 + binades[i]) << 23) | m);
+            bad += byte_one(s) + byte_one(-s);
+            n += 2;
+        }
+    }
+    const float ends[] = {0.0f, -0.0f, 0x1p120f, -0x1p120f};
+    for (unsigned i = 0; i < sizeof ends / sizeof ends[0]; ++i, ++n) bad += byte_one(ends[i]);
+    printf("byte: %ld scales x 256 codes, mismatches %ld\n", n, bad);
+    return bad;
+}
+
 int main(int argc, char **argv) {
     if (argc != 3) {
-        fprintf(stderr, "usage: %s <scale|markstein|ties|nibble> <param>\n", argv[0]);
+        fprintf(stderr, "usage: %s <scale|markstein|ties|nibble|byte> <param>\n", argv[0]);
         return 2;
     }
     const long p = atol(argv[2]);
@@ -158,6 +187,7 @@ int main(int argc, char **argv) {
     else if (!strcmp(argv[1], "markstein")) bad = check_markstein((int)p);
     else if (!strcmp(argv[1], "ties")) bad = check_ties(p);
     else if (!strcmp(argv[1], "nibble")) bad = check_nibble((int)p);
+    else if (!strcmp(argv[1], "byte")) bad = check_byte((int)p);
     else return 2;
     return bad ? 1 : 0;
 }

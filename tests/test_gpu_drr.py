@@ -313,37 +313,38 @@ def test_zero_and_negative_scales_with_negative_codes(bits_in, R):
 
 @pytest.mark.parametrize("numel", [96 * 256, 4096 * 2048 + 7 * 256])
 @pytest.mark.parametrize("R", [3, 8])
-def test_scales_on_both_sides_of_the_product_shortcut_bound(numel, R):
-    """4-bit products are formed by a shortcut that is exact only for scales
-    of magnitude 0 or in [2^-122, 2^124]; other scales take the plain product.
-    Blocks mix scales just inside and outside both ends of that range,
-    subnormal and zero scales, with arbitrary codes, on the 8- and
-    32-elements-per-lane layouts (the second size makes at least 4096 waves
-    of 2048 elements). Only input 0 gets scales near 2^124, so that every sum
-    stays finite (at most 8 * 1.5 * 2^124 + 7 * 8 * 2^118 < 2^128)."""
+@pytest.mark.parametrize("bits_in", [4, 8])
+def test_scales_on_both_sides_of_the_product_shortcut_bound(numel, R, bits_in):
+    """Products are formed by a shortcut that is exact only for scales of
+    magnitude 0 or in [2^-122, 2^124] (4-bit codes), or at most 2^120 (8-bit
+    codes); other scales take the plain product. Blocks mix scales just
+    inside and outside those ends, subnormal and zero scales, with arbitrary
+    codes, on the 8- and 32-elements-per-lane layouts (the second size makes
+    at least 4096 waves of 2048 elements). Only input 0 gets scales near the
+    upper end, so that every sum stays finite."""
     block = 256
     nb = numel // block
-    per_c = numel // 2
-    rng = np.random.default_rng([119, R, numel])
+    per_c = numel * bits_in // 8
+    rng = np.random.default_rng([119, R, numel, bits_in])
     codes = rng.integers(0, 256, R * per_c, dtype=np.uint8)
     f32 = np.float32
-    big = np.array([2.0 ** 124, np.nextafter(f32(2.0 ** 124), f32(np.inf)), -(2.0 ** 124), 1.5 * 2.0 ** 124,
-                    0.75, 0.0], f32)
-    small = np.array([2.0 ** 118, -(2.0 ** 100), 2.0 ** -122, np.nextafter(f32(2.0 ** -122), f32(0)),
+    top = f32(2.0 ** 124) if bits_in == 4 else f32(2.0 ** 120)
+    big = np.array([top, np.nextafter(top, f32(np.inf)), -top, 1.5 * top, 0.75, 0.0], f32)
+    small = np.array([2.0 ** 110, -(2.0 ** 100), 2.0 ** -122, np.nextafter(f32(2.0 ** -122), f32(0)),
                       -(2.0 ** -122), 3.0 * 2.0 ** -140, 2.0 ** -149, 2.0 ** -126, 0.0, -0.0, 0.75, -1e-3], f32)
     scales = rng.choice(small, R * nb).astype(f32)
     scales[:nb] = rng.choice(big, nb)
-    scales[: nb // 4] = f32(2.0 ** 124)                 # runs of blocks right at both ends
+    scales[: nb // 4] = top                              # runs of blocks right at both ends
     scales[nb + nb // 4: nb + nb // 2] = f32(2.0 ** -122)
     cl = [codes[r * per_c:(r + 1) * per_c] for r in range(R)]
     sl = [scales[r * nb:(r + 1) * nb] for r in range(R)]
-    for bits_out in (0, 4):
-        gco, gso, gsu = _run(codes, per_c, scales, nb, R, 4, numel, block, bits_out)
-        co, so, su = oracle.dequant_reduce_requant(cl, sl, 4, numel, block, bits_out)
+    for bits_out in (0, bits_in):
+        gco, gso, gsu = _run(codes, per_c, scales, nb, R, bits_in, numel, block, bits_out)
+        co, so, su = oracle.dequant_reduce_requant(cl, sl, bits_in, numel, block, bits_out)
         assert np.isfinite(su).all()
-        assert_bits_equal(gsu, su, f"sum across the shortcut bound R={R} n={numel}")
+        assert_bits_equal(gsu, su, f"sum across the shortcut bound R={R} n={numel} bits={bits_in}")
         if bits_out:
             assert_bits_equal(gso, so, "requantized scales")
             assert_bits_equal(gco, co, "requantized codes")
-    avg = _run_avg(codes, per_c, scales, nb, R, 4, numel, block, 7)
-    assert_bits_equal(avg, oracle.dequant_average(cl, sl, 4, numel, block, 7), "average")
+    avg = _run_avg(codes, per_c, scales, nb, R, bits_in, numel, block, 7)
+    assert_bits_equal(avg, oracle.dequant_average(cl, sl, bits_in, numel, block, 7), "average")

@@ -5,7 +5,7 @@ ZPP_EXHAUSTIVE_IDENTITIES=1 for the exhaustive ones (several minutes):
 every significand of five binades for the block-scale identity, every
 (x, absmax) pair of finite bfloat16 values for Markstein's division,
 about 3.6e9 near-tie binary32 values, and every significand of twelve
-binades for the 4-bit product shortcut.
+binades for the 4- and 8-bit product shortcuts.
 """
 from __future__ import annotations
 
@@ -47,3 +47,7 @@ def test_markstein_quotients_near_ties(exe):
 
 def test_nibble_products_by_fused_multiply_add(exe):
     _run(exe, "nibble", 1 if FULL else 997)
+
+
+def test_byte_products_by_fused_multiply_add(exe):
+    _run(exe, "byte", 8 if FULL else 4099)
