@@ -23,7 +23,9 @@
  *   its launch a call reads and clears the calling thread's pending HIP
  *   error (hipGetLastError), so an error left there by an earlier call does
  *   not survive it; a rejected launch returns ZPP_ERR_LAUNCH and leaves no
- *   error pending.
+ *   error pending. The hop reductions launch once per 2^29 output elements;
+ *   if a later launch is rejected, the earlier ones still run, so after
+ *   ZPP_ERR_LAUNCH the outputs are unspecified.
  * - The caller allocates and owns every buffer; the library allocates
  *   nothing, keeps no per-call state and may be called from several threads
  *   and streams at once. Outputs must not overlap inputs or each other
