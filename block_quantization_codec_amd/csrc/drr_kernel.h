@@ -176,12 +176,14 @@ __device__ __forceinline__ void dequant_dword(uint32_t w, float s, float s16, fl
 }
 
 // Sum one batch of loaded inputs into acc, in input order.
+// Positions from `valid` on (at least 1) are skipped: a wave-uniform branch.
 template <typename G, int NB, bool FIRST, bool FAST>
 __device__ __forceinline__ void accumulate(const uint32_t (&w)[NB][G::U][G::ND], const float (&s)[NB][G::U],
-                                           float (&acc)[G::U][G::E]) {
+                                           float (&acc)[G::U][G::E], int valid) {
     constexpr int CPW = 32 / G::BITS_IN;  // codes per dword
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
+        if (k > 0 && k >= valid) break;
 #pragma unroll
         for (int u = 0; u < G::U; ++u) {
             const float sk = s[k][u];
@@ -220,21 +222,26 @@ struct LaneOffsets {
     uint32_t scale[G::U];
 };
 
-template <typename G, int NB>
+// Inputs r0 .. r0+NB-1. PAD: positions past the last of the n_inputs inputs
+// reload it (valid addresses, unused values), so that a last, partial batch
+// issues the same loads as a full one.
+template <typename G, int NB, bool PAD>
 __device__ __forceinline__ void load_batch(const uint8_t *__restrict__ codes_in, int64_t codes_stride,
                                            const float *__restrict__ scales_in, int64_t scales_stride, int r0,
-                                           const LaneOffsets<G> &o, Batch<G, NB> &b) {
+                                           int n_inputs, const LaneOffsets<G> &o, Batch<G, NB> &b) {
     // Scales first: the batch's choice of product formula needs all of them,
     // while each input's codes are needed only when that input is summed.
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
-        const uint8_t *sc = reinterpret_cast<const uint8_t *>(scales_in + static_cast<int64_t>(r0 + k) * scales_stride);
+        const int ri = PAD ? min(r0 + k, n_inputs - 1) : r0 + k;
+        const uint8_t *sc = reinterpret_cast<const uint8_t *>(scales_in + static_cast<int64_t>(ri) * scales_stride);
 #pragma unroll
         for (int u = 0; u < G::U; ++u) b.s[k][u] = *reinterpret_cast<const float *>(sc + o.scale[u]);
     }
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
-        const uint8_t *c = codes_in + static_cast<int64_t>(r0 + k) * codes_stride;
+        const int ri = PAD ? min(r0 + k, n_inputs - 1) : r0 + k;
+        const uint8_t *c = codes_in + static_cast<int64_t>(ri) * codes_stride;
 #pragma unroll
         for (int u = 0; u < G::U; ++u) load_dwords<G::ND>(c + o.code[u], b.w[k][u]);
     }
@@ -250,7 +257,7 @@ __device__ __forceinline__ void load_batch(const uint8_t *__restrict__ codes_in,
 // finished sum before writing it (a sum that starts at +0 is never -0), and a
 // requantized sum gets the same codes and scale either way.
 template <typename G, int NB, bool FIRST>
-__device__ __forceinline__ void add_batch(const Batch<G, NB> &b, float (&acc)[G::U][G::E]) {
+__device__ __forceinline__ void add_batch(const Batch<G, NB> &b, float (&acc)[G::U][G::E], int valid = NB) {
     // Every |s| of the batch as its bit pattern without the sign, shifted
     // left by one (t), which orders like |s| with infinities and NaNs above
     // every finite value: the largest t, and the smallest t - 1, where a zero
@@ -270,27 +277,41 @@ __device__ __forceinline__ void add_batch(const Batch<G, NB> &b, float (&acc)[G:
     else
         fast = (hi <= (as_u(0x1p124f) << 1)) & (lo >= (as_u(0x1p-122f) << 1) - 1u);  // -8 s finite, s/16 exact
     if (fast)
-        accumulate<G, NB, FIRST, true>(b.w, b.s, acc);
+        accumulate<G, NB, FIRST, true>(b.w, b.s, acc, valid);
     else
-        accumulate<G, NB, FIRST, false>(b.w, b.s, acc);
+        accumulate<G, NB, FIRST, false>(b.w, b.s, acc, valid);
 }
 
-// Sum every remaining full batch of NB inputs from input r on (r advances).
-// r == 0 means no input has been summed yet.
+// Sum all n_inputs inputs in batches of NB, one batch loaded and then summed
+// at a time; the first batch starts the sums. A last, partial batch loads
+// like a full one and skips the positions past the last input. With no
+// choice of batch size there is one path through the sums, and the compiler
+// keeps them in the same registers throughout.
+template <typename G, int NB>
+__device__ __forceinline__ void consume_padded(const uint8_t *__restrict__ codes_in, int64_t codes_stride,
+                                               const float *__restrict__ scales_in, int64_t scales_stride,
+                                               int n_inputs, const LaneOffsets<G> &o, float (&acc)[G::U][G::E]) {
+    {
+        Batch<G, NB> b;
+        load_batch<G, NB, true>(codes_in, codes_stride, scales_in, scales_stride, 0, n_inputs, o, b);
+        add_batch<G, NB, true>(b, acc, n_inputs);
+    }
+    for (int r = NB; r < n_inputs; r += NB) {
+        Batch<G, NB> b;
+        load_batch<G, NB, true>(codes_in, codes_stride, scales_in, scales_stride, r, n_inputs, o, b);
+        add_batch<G, NB, false>(b, acc, n_inputs - r);
+    }
+}
+
+// Sum every remaining full batch of NB inputs from input r on (r advances)
+// into sums that already hold +0.
 template <typename G, int NB>
 __device__ __forceinline__ void consume(const uint8_t *__restrict__ codes_in, int64_t codes_stride,
                                         const float *__restrict__ scales_in, int64_t scales_stride, int n_inputs,
                                         const LaneOffsets<G> &o, int &r, float (&acc)[G::U][G::E]) {
-    if (r == 0) {
-        if (NB > n_inputs) return;
-        Batch<G, NB> b;
-        load_batch<G, NB>(codes_in, codes_stride, scales_in, scales_stride, 0, o, b);
-        add_batch<G, NB, true>(b, acc);
-        r = NB;
-    }
     for (; r + NB <= n_inputs; r += NB) {
         Batch<G, NB> b;
-        load_batch<G, NB>(codes_in, codes_stride, scales_in, scales_stride, r, o, b);
+        load_batch<G, NB, false>(codes_in, codes_stride, scales_in, scales_stride, r, n_inputs, o, b);
         add_batch<G, NB, false>(b, acc);
     }
 }
@@ -299,7 +320,7 @@ __device__ __forceinline__ void consume(const uint8_t *__restrict__ codes_in, in
 // summed, so that a wave's loads overlap its own arithmetic (two batches of
 // registers, used in turn). Every sum of a batch follows the loads of the
 // next batch without a branch in between, so the sum waits for its own
-// batch's loads only. The sums must already hold +0 (no FIRST batch).
+// batch's loads only.
 template <typename G, int NB>
 __device__ __forceinline__ void consume_overlapped(const uint8_t *__restrict__ codes_in, int64_t codes_stride,
                                                    const float *__restrict__ scales_in, int64_t scales_stride,
@@ -307,14 +328,14 @@ __device__ __forceinline__ void consume_overlapped(const uint8_t *__restrict__ c
                                                    float (&acc)[G::U][G::E]) {
     if (r + NB > n_inputs) return;
     Batch<G, NB> a, b;
-    load_batch<G, NB>(codes_in, codes_stride, scales_in, scales_stride, r, o, a);
+    load_batch<G, NB, false>(codes_in, codes_stride, scales_in, scales_stride, r, n_inputs, o, a);
     for (;;) {
         if (r + 2 * NB > n_inputs) {
             add_batch<G, NB, false>(a, acc);
             r += NB;
             return;
         }
-        load_batch<G, NB>(codes_in, codes_stride, scales_in, scales_stride, r + NB, o, b);
+        load_batch<G, NB, false>(codes_in, codes_stride, scales_in, scales_stride, r + NB, n_inputs, o, b);
         add_batch<G, NB, false>(a, acc);
         r += NB;
         if (r + 2 * NB > n_inputs) {
@@ -322,7 +343,7 @@ __device__ __forceinline__ void consume_overlapped(const uint8_t *__restrict__ c
             r += NB;
             return;
         }
-        load_batch<G, NB>(codes_in, codes_stride, scales_in, scales_stride, r + NB, o, a);
+        load_batch<G, NB, false>(codes_in, codes_stride, scales_in, scales_stride, r + NB, n_inputs, o, a);
         add_batch<G, NB, false>(b, acc);
         r += NB;
     }
@@ -365,23 +386,23 @@ __global__ __launch_bounds__(kBlockThreads) void drr_kernel(const uint8_t *__res
 
         float acc[U][E];
         // Inputs are consumed in batches whose loads are all issued before
-        // the batch is summed: full batches of RB, then of 8, then of 4, then
-        // single inputs; whichever batch comes first starts the sums. The
-        // narrow layout, whose waves are few, also overlaps each batch's
-        // loads with the previous batch's sums; its sums start from +0.
-        int r = 0;
+        // the batch is summed. The wide layout sums batches of RB, the last
+        // one padded, and its first batch starts the sums. The narrow layout,
+        // whose waves are few, starts its sums from +0 and overlaps each
+        // batch's loads with the previous batch's sums, then takes what is
+        // left four inputs and then one input at a time.
         if constexpr (G::OVERLAP) {
 #pragma unroll
             for (int u = 0; u < U; ++u)
 #pragma unroll
                 for (int i = 0; i < E; ++i) acc[u][i] = 0.0f;
+            int r = 0;
             consume_overlapped<G, G::RB>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, o, r, acc);
+            if constexpr (G::RB > 4) consume<G, 4>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, o, r, acc);
+            consume<G, 1>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, o, r, acc);
         } else {
-            consume<G, G::RB>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, o, r, acc);
+            consume_padded<G, G::RB>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, o, acc);
         }
-        if constexpr (G::RB > 8) consume<G, 8>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, o, r, acc);
-        consume<G, 4>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, o, r, acc);
-        consume<G, 1>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, o, r, acc);
 
         if (AVG || sum_out != nullptr) {
 #pragma unroll
