@@ -172,10 +172,13 @@ def test_empty_is_a_no_op():
     assert g.all_canary()
 
 
-@pytest.mark.parametrize("bits_in,bits_out,R", [(4, 4, 8), (8, 8, 3), (4, 0, 5)])
+@pytest.mark.parametrize("bits_in,bits_out,R", [(4, 4, 8), (8, 8, 3), (4, 0, 5), (8, 4, 9), (4, 8, 17),
+                                                 (8, 0, 16)])
 def test_wide_lane_path(bits_in, bits_out, R):
     """Outputs large enough for the 32-elements-per-lane layout (at least 4096 waves of
-    2048 elements), with a ragged tail; the small cases above use 8 elements per lane."""
+    2048 elements), with a ragged tail; the small cases above use 8 elements per lane.
+    That layout sums batches of 8 inputs: fewer than 8, 9 and 17 inputs end in a
+    partial batch, 8 and 16 do not; mixed code widths use their own kernels."""
     block = 256
     numel = 8192 * 2048 + 3 * 2048 + 5 * block
     rng = np.random.default_rng([R, bits_in])
