@@ -15,18 +15,19 @@
 // of contributing GPUs (one correctly rounded binary32 division): page
 // "ZeRO Stage 2: Gradient Partitioning", step 2 of the stage-2 flow, where
 // the reduce-scatter hands each GPU the average of its shard. Any code bytes
-// and scales are accepted: 4-bit products use a fused multiply-add shortcut
-// only where it is exact, and the first sum, written acc = p, is made exact by
-// adding +0 to every finished sum (see add_batch).
+// and scales are accepted: products use a fused multiply-add shortcut only
+// where it is exact (see dequant_dword), and the first sum, written acc = p,
+// is made exact by adding +0 to every finished sum (see add_batch).
 //
 // Layout of the work: a lane owns E consecutive elements of a wave segment of
 // 64 E elements: E = 32 (one 16-byte vector of 4-bit codes per input, so
 // each load instruction reads one contiguous kilobyte of an input), or E = 8
 // for small outputs, which then still spread over every SIMD. Inputs are
 // read a batch at a time, all loads of a batch in flight before the batch is
-// summed in input order; with E = 8 the next batch's loads are also issued
-// before the current batch is summed. The requantized block maximum is
-// reduced across the block's lanes with DPP / permlane swaps.
+// summed in input order. With E = 32 every batch holds 8 inputs (a last,
+// partial one skips its padding); with E = 8 the next batch's loads are also
+// issued before the current batch is summed. The requantized block maximum
+// is reduced across the block's lanes with DPP / permlane swaps.
 #pragma once
 
 #include "zpp_device.h"
@@ -212,10 +213,10 @@ struct Batch {
 };
 
 // A lane's byte offsets within one input: of its code vectors and of their
-// block scales. Input r's data then sits at a wave-uniform base (held in
-// scalar registers) plus these offsets, the same for every input, so a load
-// needs no per-input vector address. A launch covers fewer than 2^29
-// elements, so every offset fits in 32 bits.
+// block scales, the same for every input. An address is then a wave-uniform
+// base (input r's) plus a 32-bit lane offset, which the first batch of the
+// wide layout loads in the scalar-base form (global_load ... v_off, s[base]).
+// A launch covers at most 2^29 elements, so every offset fits in 32 bits.
 template <typename G>
 struct LaneOffsets {
     uint32_t code[G::U];
@@ -386,8 +387,9 @@ __global__ __launch_bounds__(kBlockThreads) void drr_kernel(const uint8_t *__res
 
         float acc[U][E];
         // Inputs are consumed in batches whose loads are all issued before
-        // the batch is summed. The wide layout sums batches of RB, the last
-        // one padded, and its first batch starts the sums. The narrow layout,
+        // the batch is summed. The wide layout sums batches of RB (a last,
+        // partial one skips its padding), and its first batch starts the
+        // sums. The narrow layout,
         // whose waves are few, starts its sums from +0 and overlaps each
         // batch's loads with the previous batch's sums, then takes what is
         // left four inputs and then one input at a time.
