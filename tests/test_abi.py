@@ -211,3 +211,17 @@ def test_oracle_and_library_share_no_code():
             assert not re.search(r"^\s*(import|from)\s+block_quantization_codec_amd", text, re.M), fn
             assert not re.search(r"#\s*include\s*[<\"].*zpp", text), fn
             assert "libzpp" not in text, fn
+
+
+def test_import_fails_loudly_without_the_library(tmp_path):
+    """The binding has no fallback: a copy of the package with no libzpp.so
+    beside it refuses to import, naming the missing library."""
+    import shutil
+    import sys
+    pkg = os.path.join(ROOT, "block_quantization_codec_amd")
+    dst = tmp_path / "block_quantization_codec_amd"
+    shutil.copytree(pkg, dst, ignore=shutil.ignore_patterns("*.so", "__pycache__", "csrc"))
+    r = subprocess.run([sys.executable, "-c", "import block_quantization_codec_amd"], cwd=tmp_path,
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "libzpp.so is missing" in r.stderr
