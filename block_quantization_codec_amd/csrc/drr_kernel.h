@@ -134,45 +134,65 @@ __device__ __forceinline__ void store_dwords(uint8_t *p, const uint32_t (&d)[ND]
     }
 }
 
+// Per-input factors of the product formulas (see dequant_dword).
+struct Factors {
+    float s;    // the scale
+    float mb;   // -2^(bits-1) s
+    float s24;  // s * 2^24 (4-bit codes)
+    float s20;  // s * 2^20 (4-bit codes)
+};
+
+template <int BITS_IN>
+__device__ __forceinline__ Factors factors_of(float s) {
+    return Factors{s, s * (BITS_IN == 8 ? -128.0f : -8.0f), s * 0x1p24f, s * 0x1p20f};
+}
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
 // The codes of dword `w` of one input as binary32 products code * s, element
 // 0 first. FAST: flipping the top bit of a two's-complement code q gives the
 // unsigned q + 2^(bits-1) (q + 8 for a nibble, q + 128 for a byte), and a
-// byte converts to binary32 in one instruction (v_cvt_f32_ubyte0..3; 4-bit
-// codes: the even nibbles masked in place give q + 8, the odd ones
-// 16 (q + 8)). A fused multiply-add with s (or s / 16) and mb = -2^(bits-1) s
-// then forms (q + 2^(bits-1)) s - 2^(bits-1) s = q s exactly and rounds it
-// once, which is the correctly rounded product whenever mb is finite and
-// s / 16 exact: s == 0 or 2^-122 <= |s| <= 2^124 for 4-bit codes, and
-// |s| <= 2^120 for 8-bit codes. An exact zero comes out as +0 where the
-// product may be -0, which no sum can tell apart: every sum starts from +0.
-// (Converting two nibbles per instruction as FP8 E4M3 bytes, exact for byte
-// values below 16, issues fewer instructions but measured slower on gfx950,
-// as did the sign-extending SDWA conversion followed by a multiply.)
+// fused multiply-add with mb = -2^(bits-1) s forms (q + 2^(bits-1)) s +
+// mb = q s exactly and rounds it once, which is the correctly rounded
+// product. 8-bit codes: each byte converts to binary32 in one instruction
+// (v_cvt_f32_ubyte0..3); exact whenever mb is finite, |s| <= 2^120. 4-bit
+// codes: a 16-bit half holding n < 1024 is the binary16 subnormal n 2^-24,
+// which v_fma_mix_f32 widens exactly inside the fused multiply-add; nibbles
+// masked into the halves, in place (n = q + 8, factor s 2^24) or four bits
+// up (n = 16 (q + 8), factor s 2^20), need no conversion instruction at all.
+// Exact whenever s 2^24 is finite: |s| <= 2^103. An exact zero comes out as
+// +0 where the product may be -0, which no sum can tell apart: every sum
+// starts from +0. (Also measured, and slower on gfx950: FP8 E4M3 decoding
+// of byte values below 16, and the sign-extending SDWA conversion followed
+// by a multiply.)
 template <int BITS_IN, bool FAST>
-__device__ __forceinline__ void dequant_dword(uint32_t w, float s, float s16, float mb, float (&p)[32 / BITS_IN]) {
+__device__ __forceinline__ void dequant_dword(uint32_t w, const Factors &f, float (&p)[32 / BITS_IN]) {
     if constexpr (BITS_IN == 8 && FAST) {
         uint32_t u = w ^ 0x80808080u;  // byte i: q_i + 128
         asm("" : "+v"(u));             // opaque: each byte converts straight from the dword
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = __builtin_fmaf(static_cast<float>((u >> (8 * i)) & 0xFFu), s, mb);
+        for (int i = 0; i < 4; ++i) p[i] = __builtin_fmaf(static_cast<float>((u >> (8 * i)) & 0xFFu), f.s, f.mb);
     } else if constexpr (BITS_IN == 8) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = static_cast<float>(static_cast<int8_t>(w >> (8 * i))) * s;
+        for (int i = 0; i < 4; ++i) p[i] = static_cast<float>(static_cast<int8_t>(w >> (8 * i))) * f.s;
     } else if constexpr (FAST) {
-        uint32_t even = (w ^ 0x88888888u) & 0x0F0F0F0Fu;  // byte i: q_2i + 8
-        uint32_t odd = (w ^ 0x88888888u) & 0xF0F0F0F0u;   // byte i: 16 (q_2i+1 + 8)
-        // Opaque to the optimizer, so that each byte converts straight from
-        // its dword instead of being extracted first.
-        asm("" : "+v"(even));
-        asm("" : "+v"(odd));
+        // Nibble j of w is element j. Halves: d0 = elements 0 | 4, d1 = 1 | 5
+        // (four bits up), d2 = 2 | 6, d3 = 3 | 7 (four bits up).
+        const uint32_t w8 = w >> 8;
+        const h2 d0 = __builtin_bit_cast(h2, (w ^ 0x88888888u) & 0x000F000Fu);
+        const h2 d1 = __builtin_bit_cast(h2, (w ^ 0x88888888u) & 0x00F000F0u);
+        const h2 d2 = __builtin_bit_cast(h2, (w8 ^ 0x00880088u) & 0x000F000Fu);
+        const h2 d3 = __builtin_bit_cast(h2, (w8 ^ 0x00880088u) & 0x00F000F0u);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            p[2 * i] = __builtin_fmaf(static_cast<float>((even >> (8 * i)) & 0xFFu), s, mb);
-            p[2 * i + 1] = __builtin_fmaf(static_cast<float>((odd >> (8 * i)) & 0xFFu), s16, mb);
+        for (int h = 0; h < 2; ++h) {
+            p[4 * h + 0] = __builtin_fmaf(static_cast<float>(d0[h]), f.s24, f.mb);
+            p[4 * h + 1] = __builtin_fmaf(static_cast<float>(d1[h]), f.s20, f.mb);
+            p[4 * h + 2] = __builtin_fmaf(static_cast<float>(d2[h]), f.s24, f.mb);
+            p[4 * h + 3] = __builtin_fmaf(static_cast<float>(d3[h]), f.s20, f.mb);
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) p[i] = static_cast<float>(code_at<4>(w, i)) * s;
+        for (int i = 0; i < 8; ++i) p[i] = static_cast<float>(code_at<4>(w, i)) * f.s;
     }
 }
 
@@ -187,12 +207,11 @@ __device__ __forceinline__ void accumulate(const uint32_t (&w)[NB][G::U][G::ND],
         if (k > 0 && k >= valid) break;
 #pragma unroll
         for (int u = 0; u < G::U; ++u) {
-            const float sk = s[k][u];
-            const float s16 = sk * 0.0625f, mb = sk * (G::BITS_IN == 8 ? -128.0f : -8.0f);
+            const Factors f = factors_of<G::BITS_IN>(s[k][u]);
 #pragma unroll
             for (int d = 0; d < G::ND; ++d) {
                 float p[CPW];
-                dequant_dword<G::BITS_IN, FAST>(w[k][u][d], sk, s16, mb, p);
+                dequant_dword<G::BITS_IN, FAST>(w[k][u][d], f, p);
 #pragma unroll
                 for (int i = 0; i < CPW; ++i) {
                     if (FIRST && k == 0)
@@ -259,24 +278,15 @@ __device__ __forceinline__ void load_batch(const uint8_t *__restrict__ codes_in,
 // requantized sum gets the same codes and scale either way.
 template <typename G, int NB, bool FIRST>
 __device__ __forceinline__ void add_batch(const Batch<G, NB> &b, float (&acc)[G::U][G::E], int valid = NB) {
-    // Every |s| of the batch as its bit pattern without the sign, shifted
-    // left by one (t), which orders like |s| with infinities and NaNs above
-    // every finite value: the largest t, and the smallest t - 1, where a zero
-    // scale wraps to the top and so never counts.
-    uint32_t hi = 0u, lo = ~0u;
+    // The largest |s| of the batch, as its bit pattern without the sign
+    // shifted left by one: that orders like |s|, with infinities and NaNs
+    // above every finite value.
+    uint32_t hi = 0u;
 #pragma unroll
     for (int k = 0; k < NB; ++k)
 #pragma unroll
-        for (int u = 0; u < G::U; ++u) {
-            const uint32_t t = as_u(b.s[k][u]) << 1;
-            hi = max(hi, t);
-            if constexpr (G::BITS_IN == 4) lo = min(lo, t - 1u);
-        }
-    bool fast;
-    if constexpr (G::BITS_IN == 8)
-        fast = hi <= (as_u(0x1p120f) << 1);  // -128 s finite
-    else
-        fast = (hi <= (as_u(0x1p124f) << 1)) & (lo >= (as_u(0x1p-122f) << 1) - 1u);  // -8 s finite, s/16 exact
+        for (int u = 0; u < G::U; ++u) hi = max(hi, as_u(b.s[k][u]) << 1);
+    const bool fast = hi <= (as_u(G::BITS_IN == 8 ? 0x1p120f : 0x1p103f) << 1);  // the shortcut is exact
     if (fast)
         accumulate<G, NB, FIRST, true>(b.w, b.s, acc, valid);
     else

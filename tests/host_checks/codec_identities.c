@@ -11,11 +11,13 @@
  *   ties       the same quotient for x within 3 ulps of (k + 1/2) s, every k,
  *              random normal s >= 2^-96: q1 == x / s bit for bit.
  *   nibble     the 4-bit products of the hop kernels: for every code q in
- *              [-8, 7] and scale s of magnitude 0 or in [2^-122, 2^124],
- *              fma(q + 8, s, -8 s) and fma(16 (q + 8), s / 16, -8 s) equal
- *              RN(q * s) (bit for bit, except that an exact zero may differ
- *              in sign), over every significand (taken with the given
- *              stride) of binades spread over that range, both signs.
+ *              [-8, 7] and scale s with |s| <= 2^103, with n = q + 8 taken
+ *              as the binary16 subnormal n 2^-24 (exact in binary32),
+ *              fma(n 2^-24, s 2^24, -8 s) and fma(16 n 2^-24, s 2^20, -8 s)
+ *              equal RN(q * s) (bit for bit, except that an exact zero may
+ *              differ in sign), over every significand (taken with the
+ *              given stride) of binades spread over that range, subnormal
+ *              ones included, both signs.
  *   byte       the same for 8-bit codes q in [-128, 127] and |s| <= 2^120:
  *              fma(q + 128, s, -128 s) equals RN(q * s).
  *
@@ -119,11 +121,11 @@ static long check_ties(long iters) {
 
 static long nibble_one(float s) {
     long bad = 0;
-    const float m8s = s * -8.0f, s16 = s * 0.0625f;
+    const float m8s = s * -8.0f, s24 = s * 0x1p24f, s20 = s * 0x1p20f;
     for (int q = -8; q <= 7; ++q) {
         const float want = (float)q * s;
-        const float a = fmaf((float)(q + 8), s, m8s);
-        const float b = fmaf((float)(16 * (q + 8)), s16, m8s);
+        const float a = fmaf(ldexpf((float)(q + 8), -24), s24, m8s);
+        const float b = fmaf(ldexpf((float)(16 * (q + 8)), -24), s20, m8s);
         if (want == 0.0f) {
             bad += (a != 0.0f) + (b != 0.0f);
         } else {
@@ -134,16 +136,18 @@ static long nibble_one(float s) {
 }
 
 static long check_nibble(int stride) {
-    static const int binades[] = {-122, -121, -100, -64, -2, -1, 0, 1, 63, 100, 122, 123};
+    static const int binades[] = {-145, -135, -127, -126, -122, -100, -64, -1, 0, 1, 63, 102};
     long bad = 0, n = 0;
     for (unsigned i = 0; i < sizeof binades / sizeof binades[0]; ++i) {
-        const uint32_t e = (uint32_t)(127 + binades[i]) << 23;
         for (uint32_t m = 0; m < (1u << 23); m += (uint32_t)stride) {
-            bad += nibble_one(f32(e | m)) + nibble_one(-f32(e | m));
+            /* binades below 2^-126 are subnormal: significand m scaled by 2^(b + 23 - 126) */
+            const float s = binades[i] < -126 ? f32(m >> (-126 - binades[i]))
+                                              : f32(((uint32_t)(127 + binades[i]) << 23) | m);
+            bad += nibble_one(s) + nibble_one(-s);
             n += 2;
         }
     }
-    const float ends[] = {0.0f, -0.0f, 0x1p124f, -0x1p124f, 0x1p-122f, -0x1p-122f};
+    const float ends[] = {0.0f, -0.0f, 0x1p103f, -0x1p103f, 0x1p-149f, -0x1p-149f};
     for (unsigned i = 0; i < sizeof ends / sizeof ends[0]; ++i, ++n) bad += nibble_one(ends[i]);
     printf("nibble: %ld scales x 16 codes x 2 forms, mismatches %ld\n", n, bad);
     return bad;

@@ -319,21 +319,23 @@ def test_zero_and_negative_scales_with_negative_codes(bits_in, R):
 @pytest.mark.parametrize("bits_in", [4, 8])
 def test_scales_on_both_sides_of_the_product_shortcut_bound(numel, R, bits_in):
     """Products are formed by a shortcut that is exact only for scales of
-    magnitude 0 or in [2^-122, 2^124] (4-bit codes), or at most 2^120 (8-bit
-    codes); other scales take the plain product. Blocks mix scales just
-    inside and outside those ends, subnormal and zero scales, with arbitrary
-    codes, on the 8- and 32-elements-per-lane layouts (the second size makes
-    at least 4096 waves of 2048 elements). Only input 0 gets scales near the
-    upper end, so that every sum stays finite."""
+    magnitude at most 2^103 (4-bit codes) or 2^120 (8-bit codes); larger
+    ones take the plain product. Blocks mix scales just inside and outside
+    that bound with tiny (down to the smallest subnormal), zero and negative
+    scales and arbitrary codes, on the 8- and 32-elements-per-lane layouts
+    (the second size makes at least 4096 waves of 2048 elements). Only input
+    0 gets scales near the bound and above it, and those stay at most
+    1.5 * 2^124, so that every sum stays finite."""
     block = 256
     nb = numel // block
     per_c = numel * bits_in // 8
     rng = np.random.default_rng([119, R, numel, bits_in])
     codes = rng.integers(0, 256, R * per_c, dtype=np.uint8)
     f32 = np.float32
-    top = f32(2.0 ** 124) if bits_in == 4 else f32(2.0 ** 120)
-    big = np.array([top, np.nextafter(top, f32(np.inf)), -top, 1.5 * top, 0.75, 0.0], f32)
-    small = np.array([2.0 ** 110, -(2.0 ** 100), 2.0 ** -122, np.nextafter(f32(2.0 ** -122), f32(0)),
+    top = f32(2.0 ** 103) if bits_in == 4 else f32(2.0 ** 120)
+    far = f32(2.0 ** 124) if bits_in == 4 else f32(1.25 * 2.0 ** 120)   # well above the bound, sums finite
+    big = np.array([top, np.nextafter(top, f32(np.inf)), -top, 1.5 * top, far, 0.75, 0.0], f32)
+    small = np.array([2.0 ** 90, -(2.0 ** 100), 2.0 ** -122, np.nextafter(f32(2.0 ** -122), f32(0)),
                       -(2.0 ** -122), 3.0 * 2.0 ** -140, 2.0 ** -149, 2.0 ** -126, 0.0, -0.0, 0.75, -1e-3], f32)
     scales = rng.choice(small, R * nb).astype(f32)
     scales[:nb] = rng.choice(big, nb)

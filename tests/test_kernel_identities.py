@@ -5,7 +5,7 @@ ZPP_EXHAUSTIVE_IDENTITIES=1 for the exhaustive ones (several minutes):
 every significand of five binades for the block-scale identity, every
 (x, absmax) pair of finite bfloat16 values for Markstein's division,
 about 3.6e9 near-tie binary32 values, and every significand of twelve
-binades for the 4- and 8-bit product shortcuts.
+binades (subnormal ones included) for the 4- and 8-bit product shortcuts.
 """
 from __future__ import annotations
 
