@@ -97,6 +97,14 @@ def test_input_counts(R, bits_in, bits_out):
     _check(R, bits_in, bits_out, 256, 256 * 100, 1)
 
 
+@pytest.mark.parametrize("R", [257, 4096])
+@pytest.mark.parametrize("bits_in,bits_out", [(4, 4), (8, 0)])
+def test_many_inputs(R, bits_in, bits_out):
+    """Up to the largest input count the entry point accepts (4096): many
+    overlapped batches of 8, then the batch of 4 and single inputs."""
+    _check(R, bits_in, bits_out, 256, 256 * 3, 7)
+
+
 @pytest.mark.parametrize("block", BLOCKS)
 @pytest.mark.parametrize("bits_in,bits_out", [(4, 4), (8, 8), (4, 8), (8, 4)])
 def test_block_sizes(block, bits_in, bits_out):
