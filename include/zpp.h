@@ -178,9 +178,9 @@ zpp_status zpp_reorder_slices(const void *in, void *out, int64_t slice_bytes, in
  * The fused hop step of qgZ [QGZ]: dequantize n_inputs received pieces,
  * sum them in binary32 in ascending input order (each product and each sum
  * rounded on its own: no product is fused into the sum), and either
- * requantize the sum
- * for the next hop (hop 1, intra-node reduction) or emit it as binary32
- * (hop 2, the owner's reduced shard [RS]). It sums; it does not average.
+ * requantize the sum for the next hop (hop 1, intra-node reduction) or emit
+ * it as binary32 (hop 2, the owner's reduced shard [RS]). It sums; it does
+ * not average.
  *
  *   codes_in            in   input r's codes at codes_in + r*codes_stride_bytes
  *   codes_stride_bytes  in   >= 0, multiple of 16
