@@ -41,6 +41,7 @@ ZPP_MIN_BLOCK = 32
 ZPP_MAX_BLOCK = 4096
 ZPP_MAX_INPUTS = 4096
 ZPP_MAX_DIVISOR = 1 << 24
+ZPP_MAX_NUMEL = 1 << 40
 
 EXPORTED = ("zpp_quantize_blocks", "zpp_quantize_reordered", "zpp_dequantize_blocks", "zpp_reorder_slices",
             "zpp_dequant_reduce_requant", "zpp_dequant_reduce_average", "zpp_status_string", "zpp_abi_version")

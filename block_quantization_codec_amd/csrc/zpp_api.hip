@@ -153,7 +153,7 @@ zpp_status zpp_quantize_blocks(const void *x, zpp_dtype x_dtype, int64_t numel, 
                                void *codes, float *scales, void *stream) {
     if (x_dtype != ZPP_BF16 && x_dtype != ZPP_FP32) return ZPP_ERR_ARG;
     if (bits != 8 && bits != 4) return ZPP_ERR_ARG;
-    if (!is_pow2_block(block) || numel < 0 || numel % block != 0) return ZPP_ERR_ARG;
+    if (!is_pow2_block(block) || numel < 0 || numel > ZPP_MAX_NUMEL || numel % block != 0) return ZPP_ERR_ARG;
     if (numel == 0) return ZPP_OK;
     if (!x || !codes || !scales) return ZPP_ERR_NULL;
     if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4)) return ZPP_ERR_ALIGN;
@@ -178,7 +178,7 @@ zpp_status zpp_quantize_reordered(const void *x, zpp_dtype x_dtype, int64_t slic
     if (n > 65535) return ZPP_ERR_ARG;
     if (!is_pow2_block(block) || slice_elems < 0 || slice_elems % block != 0) return ZPP_ERR_ARG;
     if (first_slice < 0 || n_slices < 0 || first_slice + static_cast<int64_t>(n_slices) > n) return ZPP_ERR_ARG;
-    if (slice_elems > (INT64_C(1) << 40) / n) return ZPP_ERR_ARG;
+    if (slice_elems > ZPP_MAX_NUMEL / n) return ZPP_ERR_ARG;
     if (slice_elems == 0 || n_slices == 0) return ZPP_OK;
     if (!x || !codes || !scales) return ZPP_ERR_NULL;
     if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4)) return ZPP_ERR_ALIGN;
@@ -198,7 +198,7 @@ zpp_status zpp_dequantize_blocks(const void *codes, const float *scales, int32_t
                                  void *y, zpp_dtype y_dtype, void *stream) {
     if (y_dtype != ZPP_BF16 && y_dtype != ZPP_FP32) return ZPP_ERR_ARG;
     if (bits != 8 && bits != 4) return ZPP_ERR_ARG;
-    if (!is_pow2_block(block) || numel < 0 || numel % block != 0) return ZPP_ERR_ARG;
+    if (!is_pow2_block(block) || numel < 0 || numel > ZPP_MAX_NUMEL || numel % block != 0) return ZPP_ERR_ARG;
     if (numel == 0) return ZPP_OK;
     if (!codes || !scales || !y) return ZPP_ERR_NULL;
     if (!aligned(codes, 16) || !aligned(y, 16) || !aligned(scales, 4)) return ZPP_ERR_ALIGN;
@@ -218,7 +218,7 @@ zpp_status zpp_reorder_slices(const void *in, void *out, int64_t slice_bytes, in
     if (n_nodes < 1 || gpus_per_node < 1 || slice_bytes < 0) return ZPP_ERR_ARG;
     if (static_cast<int64_t>(n_nodes) * gpus_per_node > 65535) return ZPP_ERR_ARG;
     const int64_t n = static_cast<int64_t>(n_nodes) * gpus_per_node;
-    if (slice_bytes > INT64_MAX / n) return ZPP_ERR_ARG;
+    if (slice_bytes > 4 * ZPP_MAX_NUMEL / n) return ZPP_ERR_ARG;
     if (slice_bytes == 0) return ZPP_OK;
     if (!in || !out) return ZPP_ERR_NULL;
     const Range ri{in, slice_bytes * n}, ro{out, slice_bytes * n};
@@ -236,9 +236,10 @@ zpp_status zpp_dequant_reduce_requant(const void *codes_in, int64_t codes_stride
                                       float *sum_out, void *stream) {
     if (bits_in != 8 && bits_in != 4) return ZPP_ERR_ARG;
     if (bits_out != 0 && bits_out != 8 && bits_out != 4) return ZPP_ERR_ARG;
-    if (!is_pow2_block(block) || numel < 0 || numel % block != 0) return ZPP_ERR_ARG;
+    if (!is_pow2_block(block) || numel < 0 || numel > ZPP_MAX_NUMEL || numel % block != 0) return ZPP_ERR_ARG;
     if (n_inputs < 1 || n_inputs > ZPP_MAX_INPUTS) return ZPP_ERR_ARG;
-    if (codes_stride_bytes < 0 || scales_stride < 0) return ZPP_ERR_ARG;
+    if (codes_stride_bytes < 0 || codes_stride_bytes > ZPP_MAX_NUMEL) return ZPP_ERR_ARG;
+    if (scales_stride < 0 || scales_stride > ZPP_MAX_NUMEL) return ZPP_ERR_ARG;
     if (bits_out == 0 && (codes_out || scales_out)) return ZPP_ERR_ARG;
     if (bits_out == 0 && !sum_out) return ZPP_ERR_ARG;
     if (numel == 0) return ZPP_OK;
@@ -270,9 +271,10 @@ zpp_status zpp_dequant_reduce_average(const void *codes_in, int64_t codes_stride
                                       int64_t scales_stride, int32_t n_inputs, int32_t bits_in, int64_t numel,
                                       int32_t block, int32_t divisor, float *avg_out, void *stream) {
     if (bits_in != 8 && bits_in != 4) return ZPP_ERR_ARG;
-    if (!is_pow2_block(block) || numel < 0 || numel % block != 0) return ZPP_ERR_ARG;
+    if (!is_pow2_block(block) || numel < 0 || numel > ZPP_MAX_NUMEL || numel % block != 0) return ZPP_ERR_ARG;
     if (n_inputs < 1 || n_inputs > ZPP_MAX_INPUTS) return ZPP_ERR_ARG;
-    if (codes_stride_bytes < 0 || scales_stride < 0) return ZPP_ERR_ARG;
+    if (codes_stride_bytes < 0 || codes_stride_bytes > ZPP_MAX_NUMEL) return ZPP_ERR_ARG;
+    if (scales_stride < 0 || scales_stride > ZPP_MAX_NUMEL) return ZPP_ERR_ARG;
     if (divisor < 1 || divisor > ZPP_MAX_DIVISOR) return ZPP_ERR_ARG;
     if (numel == 0) return ZPP_OK;
     if (!codes_in || !scales_in || !avg_out) return ZPP_ERR_NULL;

@@ -36,9 +36,9 @@
  *   are two's-complement nibbles, element 2i in the low nibble of byte i.
  *   `scales` holds numel/B binary32 scales s_b (the scale itself, not its
  *   inverse). An element's value is code * s_b.
- * - B is a power of two in [ZPP_MIN_BLOCK, ZPP_MAX_BLOCK]; numel >= 0 and
- *   numel % B == 0 (callers pad; zero padding changes no scale and no sum).
- *   numel == 0 is a no-op returning ZPP_OK.
+ * - B is a power of two in [ZPP_MIN_BLOCK, ZPP_MAX_BLOCK]; 0 <= numel <=
+ *   ZPP_MAX_NUMEL and numel % B == 0 (callers pad; zero padding changes no
+ *   scale and no sum). numel == 0 is a no-op returning ZPP_OK.
  * - Alignment: element data and code pointers 16-byte aligned, scale
  *   pointers 4-byte aligned (ZPP_ERR_ALIGN otherwise).
  *
@@ -78,6 +78,11 @@ extern "C" {
 #define ZPP_MAX_BLOCK 4096
 #define ZPP_MAX_INPUTS 4096
 #define ZPP_MAX_DIVISOR 16777216 /* 2^24: every divisor up to it is exact in binary32 */
+/* 2^40: the largest element count, input stride (bytes for codes, floats
+ * for scales), and reordered buffer (elements, or bytes / 4) accepted; far
+ * beyond any GPU's memory, it keeps every byte range of a call exact in
+ * 64-bit arithmetic (larger values: ZPP_ERR_ARG). */
+#define ZPP_MAX_NUMEL ((int64_t)1 << 40)
 
 typedef enum zpp_status {
     ZPP_OK = 0,
@@ -101,7 +106,7 @@ typedef enum zpp_dtype {
  * (the one-shot 4-bit gradient quantization before the all-to-all).
  *
  *   x        in   numel elements of x_dtype (ZPP_BF16 or ZPP_FP32), 16-B aligned
- *   numel    in   element count, multiple of `block`
+ *   numel    in   element count, multiple of `block`, <= ZPP_MAX_NUMEL
  *   block    in   block size B (power of two, 32..4096)
  *   bits     in   8 or 4
  *   codes    out  numel*bits/8 bytes, 16-B aligned
@@ -127,7 +132,7 @@ zpp_status zpp_quantize_blocks(const void *x, zpp_dtype x_dtype, int64_t numel,
  * caller quantize the chunk it keeps straight into its receive buffer.
  *
  *   x               in   N * slice_elems elements of x_dtype, 16-B aligned
- *   slice_elems     in   multiple of `block`
+ *   slice_elems     in   multiple of `block`; N * slice_elems <= ZPP_MAX_NUMEL
  *   n_nodes, gpus_per_node  in  >= 1 each, product <= 65535
  *   first_slice, n_slices   in  0 <= first_slice, first_slice + n_slices <= N
  *   block, bits     in   as zpp_quantize_blocks
@@ -147,7 +152,7 @@ zpp_status zpp_quantize_reordered(const void *x, zpp_dtype x_dtype, int64_t slic
  *   codes    in   numel*bits/8 bytes, 16-B aligned
  *   scales   in   numel/block floats, 4-B aligned
  *   bits     in   8 or 4 (any code value is accepted, including -128 / -8)
- *   numel    in   element count, multiple of `block`
+ *   numel    in   element count, multiple of `block`, <= ZPP_MAX_NUMEL
  *   block    in   block size B
  *   y        out  numel elements of y_dtype (ZPP_BF16 or ZPP_FP32), 16-B aligned
  *   stream   in   hipStream_t
@@ -167,7 +172,8 @@ zpp_status zpp_dequantize_blocks(const void *codes, const float *scales, int32_t
  * quantization when every slice is a whole number of blocks.
  *
  *   in, out      in/out  N * slice_bytes bytes each, out-of-place
- *   slice_bytes  in      >= 0; any value (vector width adapts to alignment)
+ *   slice_bytes  in      >= 0; any value (vector width adapts to alignment);
+ *                        N * slice_bytes <= 4 * ZPP_MAX_NUMEL
  *   n_nodes, gpus_per_node  in  >= 1 each, product <= 65535
  *   stream       in      hipStream_t
  */
@@ -183,12 +189,12 @@ zpp_status zpp_reorder_slices(const void *in, void *out, int64_t slice_bytes, in
  * not average.
  *
  *   codes_in            in   input r's codes at codes_in + r*codes_stride_bytes
- *   codes_stride_bytes  in   >= 0, multiple of 16
+ *   codes_stride_bytes  in   0..ZPP_MAX_NUMEL, multiple of 16
  *   scales_in           in   input r's scales at scales_in + r*scales_stride
- *   scales_stride       in   >= 0, in floats
+ *   scales_stride       in   0..ZPP_MAX_NUMEL, in floats
  *   n_inputs            in   1..ZPP_MAX_INPUTS
  *   bits_in             in   8 or 4
- *   numel, block        in   elements per input and block size B (same B for
+ *   numel, block        in   elements per input (<= ZPP_MAX_NUMEL) and block size B (same B for
  *                            the inputs and the requantized output)
  *   codes_out, scales_out, bits_out
  *                       out  requantized sum (bits_out 8 or 4), or

@@ -197,6 +197,49 @@ def test_drr_average_argument_errors(z):
     assert call(n=0, av=None) == z.ZPP_OK
 
 
+def test_sizes_beyond_the_limit_are_refused(z):
+    """Element counts, strides and reordered buffers past ZPP_MAX_NUMEL are
+    refused before any byte range is computed, so no 64-bit product can wrap
+    round to a small or negative size; the limit itself passes (these calls
+    then stop at the overlap check, which needs no GPU)."""
+    L, M = z.library(), z.ZPP_MAX_NUMEL
+    q, d = L.zpp_quantize_blocks, L.zpp_dequantize_blocks
+    for n in (M + 256, 1 << 62, (1 << 63) - 256):
+        assert q(A, 1, n, 256, 8, A + 4096, A + 8192, None) == z.ZPP_ERR_ARG
+        assert d(A, A + 4096, 4, n, 256, A + 8192, 1, None) == z.ZPP_ERR_ARG
+    assert q(A, 1, M, 256, 8, A + 4096, A + 8192, None) == z.ZPP_ERR_OVERLAP
+    assert d(A, A + 4096, 4, M, 256, A + 8192, 1, None) == z.ZPP_ERR_OVERLAP
+
+    qr = L.zpp_quantize_reordered
+    assert qr(A, 1, (M // 8) + 256, 2, 4, 0, 8, 256, 4, A + 64, A + 128, None) == z.ZPP_ERR_ARG
+    assert qr(A, 1, 1 << 60, 2, 4, 0, 8, 256, 4, A + 64, A + 128, None) == z.ZPP_ERR_ARG
+    assert qr(A, 1, M // 8, 2, 4, 0, 8, 256, 4, A + 64, A + 128, None) == z.ZPP_ERR_OVERLAP
+
+    r = L.zpp_reorder_slices
+    assert r(A, A + 64, (4 * M) // 8 + 1, 2, 4, None) == z.ZPP_ERR_ARG
+    assert r(A, A + 64, 1 << 61, 2, 4, None) == z.ZPP_ERR_ARG
+    assert r(A, A + 64, (4 * M) // 8, 2, 4, None) == z.ZPP_ERR_OVERLAP
+
+    f, g = L.zpp_dequant_reduce_requant, L.zpp_dequant_reduce_average
+    C, S, O, OS, U = A, A + (1 << 24), A + (1 << 25), A + (1 << 26), A + (1 << 27)
+
+    def drr(n=1 << 12, cs=1 << 16, ss=1 << 10, co=O):
+        return f(C, cs, S, ss, 4, 4, n, 256, co, OS, 4, U, None)
+
+    def avg(n=1 << 12, cs=1 << 16, ss=1 << 10, av=U):
+        return g(C, cs, S, ss, 32, 4, n, 256, 256, av, None)
+
+    for call, out in ((drr, "co"), (avg, "av")):
+        assert call(n=M + 256) == z.ZPP_ERR_ARG
+        assert call(n=1 << 62) == z.ZPP_ERR_ARG
+        assert call(cs=M + 16) == z.ZPP_ERR_ARG
+        assert call(cs=(1 << 63) - 16) == z.ZPP_ERR_ARG
+        assert call(ss=M + 1) == z.ZPP_ERR_ARG
+        assert call(ss=1 << 62) == z.ZPP_ERR_ARG
+        # at the limits every range stays exact: the output inside the inputs is still seen
+        assert call(n=M, cs=M, ss=M, **{out: C + 64}) == z.ZPP_ERR_OVERLAP
+
+
 def test_oracle_and_library_share_no_code():
     """The product sources never mention the oracle, and the oracle never the product."""
     pkg = os.path.join(ROOT, "block_quantization_codec_amd")
