@@ -29,7 +29,8 @@ longest row is reported against the HBM roofline. Timed after the steps and
 reported beside them: the unfused pair (standalone reorder of the bf16
 bucket, then quantize of the reordered buffer), the other unfused order
 (quantize the bucket as it is, then reorder its codes and scales), and hop 2
-writing the averaged shard. The CPU baseline runs the plain C oracle (single thread) over
+writing the averaged shard, and a plain 1 GiB device copy (the slice reorder
+with one slice) that each row is also compared with (`copy_frac`). The CPU baseline runs the plain C oracle (single thread) over
 the same work as one step (the reorder and the quantize as two oracle steps),
 twice.
 
@@ -281,6 +282,30 @@ def time_rows(torch, stream, fns, table, K):
         out[name] = {"ms": round(ms, 5),
                      "hbm_frac": round((rin + wout) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
     return out
+
+
+def copy_ceiling(torch, z, stream, K):
+    """A plain device copy through the library's own slice reorder (one slice
+    of 1 GiB: non-temporal 16-byte loads, streaming stores), timed with HIP
+    events over K launches: the practical read + write rate the codec
+    kernels are compared with beside the 8 TB/s peak."""
+    n = 1 << 30
+    src = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        z.zpp_reorder_slices(src, dst, n, 1, 1)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(stream)
+        z.zpp_reorder_slices(src, dst, n, 1, 1)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / K
+    del src, dst
+    gbps = 2 * n / (ms * 1e-3) / 1e9
+    return {"what": "zpp_reorder_slices over one 1 GiB slice (a plain copy)", "rocprof_name": "reorder_kernel<16>",
+            "bytes": 2 * n, "ms": round(ms, 5), "GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
 
 
 def cpu_baseline(step: "Step", frac: float = 1.0, passes: int = 2):
@@ -629,6 +654,7 @@ def main() -> int:
     # pair, and hop 2 writing the averaged (optimizer-ready) shard
     unfused = time_rows(torch, stream, step.unfused_launches(), step.unfused_kernels, K)
     extra = time_rows(torch, stream, step.extra_launches(), step.extra_kernels, K)
+    copy = copy_ceiling(torch, z, stream, K)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -662,8 +688,10 @@ def main() -> int:
         "hbm_frac_step": round(total_rw / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "kernels": {p[0]: {"ms": round(p[5], 5), **spread[p[0]], "in_GBps": round(p[2] / (p[5] * 1e-3) / 1e9, 1),
                            "rw_GBps": round((p[2] + p[3]) / (p[5] * 1e-3) / 1e9, 1),
-                           "hbm_frac": round((p[2] + p[3]) / (p[5] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+                           "hbm_frac": round((p[2] + p[3]) / (p[5] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                           "copy_frac": round((p[2] + p[3]) / (p[5] * 1e-3) / 1e9 / copy["GBps"], 4)}
                     for p in per},
+        "copy_ceiling": copy,
         "unfused_reorder_then_quantize": unfused,
         "beside_the_step": extra,
         "roofline": roofline,
