@@ -166,12 +166,18 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}: bf16 or fp32 expected")
 
 
+def _need_contiguous(**tensors) -> None:
+    """The kernels read flat buffers from data_ptr(): a strided view would be misread."""
+    for name, t in tensors.items():
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
 def quantize(x, block: int, bits: int, stream=None):
     """Block-quantize a contiguous bf16/fp32 device tensor. Returns (codes uint8, scales fp32)."""
     import torch
 
-    if not x.is_contiguous():
-        raise ValueError("x must be contiguous")
+    _need_contiguous(x=x)
     n = x.numel()
     codes = torch.empty(n * bits // 8, dtype=torch.uint8, device=x.device)
     scales = torch.empty(n // block, dtype=torch.float32, device=x.device)
@@ -186,6 +192,7 @@ def quantize_reordered(x, n_nodes: int, gpus_per_node: int, block: int, bits: in
     [first_slice, first_slice + n_slices)."""
     import torch
 
+    _need_contiguous(x=x)
     n = n_nodes * gpus_per_node
     if x.numel() % n:
         raise ValueError("tensor does not split into equal slices")
@@ -203,6 +210,7 @@ def dequantize(codes, scales, bits: int, numel: int, block: int, dtype=None, str
     """Rebuild ``numel`` values (bf16 by default, or fp32) from codes and scales."""
     import torch
 
+    _need_contiguous(codes=codes, scales=scales)
     dtype = dtype or torch.bfloat16
     y = torch.empty(numel, dtype=dtype, device=codes.device)
     zpp_dequantize_blocks(codes, scales, bits, numel, block, y, _dtype_code(y), stream)
@@ -213,6 +221,7 @@ def reorder(t, n_nodes: int, gpus_per_node: int, stream=None):
     """Reorder the n_nodes*gpus_per_node equal slices of a contiguous device tensor."""
     import torch
 
+    _need_contiguous(t=t)
     n = n_nodes * gpus_per_node
     nbytes = t.numel() * t.element_size()
     if nbytes % n:
@@ -230,6 +239,7 @@ def dequant_reduce_requant(codes_in, scales_in, n_inputs: int, bits_in: int, num
     with None for outputs not requested."""
     import torch
 
+    _need_contiguous(codes_in=codes_in, scales_in=scales_in)
     dev = codes_in.device
     cs = codes_stride_bytes if codes_stride_bytes is not None else numel * bits_in // 8
     ss = scales_stride if scales_stride is not None else numel // block
@@ -250,6 +260,7 @@ def dequant_reduce_average(codes_in, scales_in, n_inputs: int, bits_in: int, num
     (the number of contributing GPUs). Returns the fp32 average."""
     import torch
 
+    _need_contiguous(codes_in=codes_in, scales_in=scales_in)
     cs = codes_stride_bytes if codes_stride_bytes is not None else numel * bits_in // 8
     ss = scales_stride if scales_stride is not None else numel // block
     avg = torch.empty(numel, dtype=torch.float32, device=codes_in.device)

@@ -240,6 +240,24 @@ def test_sizes_beyond_the_limit_are_refused(z):
         assert call(n=M, cs=M, ss=M, **{out: C + 64}) == z.ZPP_ERR_OVERLAP
 
 
+def test_helpers_refuse_strided_views(z):
+    """The allocating helpers hand data_ptr() to flat-buffer kernels, so a
+    strided view is refused before any call (no GPU needed to see it)."""
+    import torch
+
+    t = torch.zeros(64, 64).t()
+    c = torch.zeros(64, 64, dtype=torch.uint8)[:, ::2]
+    s = torch.zeros(8, 8)[:, ::2]
+    calls = [lambda: z.quantize(t, 32, 8), lambda: z.quantize_reordered(t, 2, 2, 32, 4),
+             lambda: z.dequantize(c, torch.zeros(64), 8, 2048, 32),
+             lambda: z.dequantize(torch.zeros(2048, dtype=torch.uint8), s, 8, 1024, 32),
+             lambda: z.reorder(t, 2, 2), lambda: z.dequant_reduce_requant(c, torch.zeros(64), 2, 8, 1024, 32),
+             lambda: z.dequant_reduce_average(torch.zeros(2048, dtype=torch.uint8), s, 2, 8, 1024, 32, 2)]
+    for call in calls:
+        with pytest.raises(ValueError, match="contiguous"):
+            call()
+
+
 def test_oracle_and_library_share_no_code():
     """The product sources never mention the oracle, and the oracle never the product."""
     pkg = os.path.join(ROOT, "block_quantization_codec_amd")
