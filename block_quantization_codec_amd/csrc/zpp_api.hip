@@ -48,10 +48,15 @@ int device_cus() {
 #define ZPP_GRID_CAP_PER_CU 0
 #endif
 
+// A launch's work-items (workgroups x 256) must fit in 32 bits. Past that
+// many tiles (2^35 elements for dequantize, 2^36 for the bf16 quantizers)
+// the waves take further tiles in their grid-stride loops.
+constexpr int64_t kMaxGridBlocks = INT64_C(0xFFFFFFFF) / kBlockThreads;
+
 int stream_grid(int64_t tiles) {
     const int64_t want = (tiles + (kBlockThreads / kWave) - 1) / (kBlockThreads / kWave);
     int64_t cap = static_cast<int64_t>(ZPP_GRID_CAP_PER_CU) * device_cus();
-    if (cap <= 0 || cap > 0x7FFFFFFF) cap = 0x7FFFFFFF;
+    if (cap <= 0 || cap > kMaxGridBlocks) cap = kMaxGridBlocks;
     const int64_t g = want < cap ? want : cap;
     return static_cast<int>(g < 1 ? 1 : g);
 }

@@ -8,6 +8,12 @@ compared with the oracle on sampled blocks (the first and last blocks, the
 blocks around element 2^31 and around every multiple of 2^29, where the hop
 reduction starts another launch, and random ones); blocks are independent, so
 the oracle recomputes exactly those from the same input values.
+
+Two more tests go past the largest grid one launch can have (2^32 - 1
+work-items, 16,777,215 workgroups of 256): dequantize past 2^35 elements (a
+32 GiB int8 input, 64 GiB of bf16 out) and the bf16 4-bit quantize past 2^36
+(128 GiB in), where waves take a second tile in their grid-stride loops. They
+check the blocks on both sides of the first tile no first-pass wave covers.
 """
 from __future__ import annotations
 
@@ -121,3 +127,83 @@ def test_hop_reduce_and_average_past_2_31(x):
     oav = oracle.dequant_average(ci, si, 4, idx.size * block, block, 6)
     assert_bits_equal(_gather_rows(avg, block, idx), oav, "average over 6")
     del codes, scales, co, so, su, avg
+
+
+GRID_WAVES = (0xFFFFFFFF // 256) * 4   # waves of the largest single-pass grid
+
+
+def _free():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _rows_by_copies(t, width: int, idx: np.ndarray) -> np.ndarray:
+    """Rows idx of t viewed as [-1, width], read back with plain slice copies
+    (runs of consecutive rows at a time). torch's index gather kernel faulted
+    when it gathered rows of a 32 GiB tensor, so tensors this large are never
+    indexed with an index tensor here."""
+    idx = np.asarray(idx, dtype=np.int64)
+    breaks = np.flatnonzero(np.diff(idx) != 1) + 1
+    parts = []
+    for run in np.split(idx, breaks):
+        a, b = int(run[0]), int(run[-1]) + 1
+        assert 0 <= a and b * width <= t.numel(), (a, b, width, t.numel())
+        parts.append(host(t[a * width:b * width]))
+    return np.concatenate(parts)
+
+
+def _big_sample(nb: int, boundary_block: int, seed: int) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    idx = np.unique(np.concatenate([np.arange(16), np.arange(nb - 16, nb),
+                                    np.arange(boundary_block - 32, boundary_block + 32),
+                                    rng.choice(nb, 2000, replace=False)]))
+    return idx[(idx >= 0) & (idx < nb)]
+
+
+def test_dequantize_past_the_largest_grid():
+    need_gpu()
+    import block_quantization_codec_amd as z
+    block = 256
+    n = (1 << 35) + 5 * block                       # one-pass grid covers GRID_WAVES * 512 elements
+    first_second_pass = GRID_WAVES * 512
+    assert first_second_pass < n
+    print(f"dequantize int8 -> bf16, {n} elements (tile {first_second_pass} starts the second pass)", flush=True)
+    gen = torch.Generator(device="cuda").manual_seed(41)
+    codes = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda", generator=gen)
+    e = torch.randint(-30, 31, (n // block,), device="cuda", generator=gen).float()
+    scales = torch.exp2(e) * (1.0 + torch.rand(n // block, device="cuda", generator=gen))
+    del e
+    y = z.dequantize(codes, scales, 8, n, block, dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    idx = _big_sample(n // block, first_second_pass // block, 43)
+    cs = _rows_by_copies(codes, block, idx)
+    ss = _rows_by_copies(scales, 1, idx)
+    want = oracle.dequantize(cs, ss, 8, idx.size * block, block, out="bf16")
+    assert_bits_equal(_rows_by_copies(y, block, idx), want, "bf16 dequantized past the largest grid")
+    del codes, scales, y
+    _free()
+
+
+def test_quantize_past_the_largest_grid():
+    need_gpu()
+    import block_quantization_codec_amd as z
+    block = 128
+    n = (1 << 36) + 3 * 1024                        # one-pass grid covers GRID_WAVES * 1024 elements
+    first_second_pass = GRID_WAVES * 1024
+    assert first_second_pass < n
+    print(f"quantize bf16 -> int4, {n} elements (tile {first_second_pass} starts the second pass)", flush=True)
+    gen = torch.Generator(device="cuda").manual_seed(47)
+    x = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    parts = 64
+    step = (n + parts - 1) // parts
+    for k in range(parts):  # normal values, a power-of-two scale per part
+        x[k * step:(k + 1) * step].normal_(generator=gen).mul_(2.0 ** ((k % 9) - 4))
+    codes, scales = z.quantize(x, block, 4)
+    torch.cuda.synchronize()
+    idx = _big_sample(n // block, first_second_pass // block, 53)
+    xs = _rows_by_copies(x, block, idx)
+    oc, os_ = oracle.quantize(xs, block, 4)
+    assert_bits_equal(_rows_by_copies(codes, block // 2, idx), oc, "int4 codes past the largest grid")
+    assert_bits_equal(_rows_by_copies(scales, 1, idx), os_, "int4 scales past the largest grid")
+    del x, codes, scales
+    _free()
