@@ -81,6 +81,12 @@ def codes_nbytes(numel: int, bits: int) -> int:
     return numel * bits // 8
 
 
+def _need(have: int, need: int, what: str) -> None:
+    """The C routines read as much as numel implies: shorter arrays are refused here."""
+    if have < need:
+        raise ValueError(f"{what} holds {have} items, the call needs {need}")
+
+
 def quantize(x: np.ndarray, block: int, bits: int):
     """Block-quantize ``x`` (uint16 bf16 bits or float32). Returns (codes uint8, scales float32)."""
     x = np.ascontiguousarray(x)
@@ -102,6 +108,9 @@ def dequantize(codes: np.ndarray, scales: np.ndarray, bits: int, numel: int, blo
     """Dequantize to float32 (``out='f32'``) or bf16 bit patterns (``out='bf16'``)."""
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     scales = np.ascontiguousarray(scales, dtype=np.float32)
+    if block > 0:
+        _need(codes.size, codes_nbytes(numel, bits), "codes")
+        _need(scales.size, numel // block, "scales")
     if out == "f32":
         y = np.empty(numel, dtype=np.float32)
         rc = lib().oracle_dequantize_f32(_ptr(codes), _ptr(scales), bits, numel, block, _ptr(y))
@@ -137,6 +146,9 @@ def dequant_sum(codes_list, scales_list, bits: int, numel: int, block: int) -> n
     """Sum of the inputs' dequantized values, in input order (binary32)."""
     codes = np.stack([np.ascontiguousarray(c, dtype=np.uint8) for c in codes_list])
     scales = np.stack([np.ascontiguousarray(s, dtype=np.float32) for s in scales_list])
+    if block > 0:
+        _need(codes.shape[1], codes_nbytes(numel, bits), "each input's codes")
+        _need(scales.shape[1], numel // block, "each input's scales")
     out = np.empty(numel, dtype=np.float32)
     rc = lib().oracle_dequant_sum(_ptr(codes), codes.shape[1], _ptr(scales), scales.shape[1],
                                   len(codes_list), bits, numel, block, _ptr(out))
@@ -150,6 +162,9 @@ def dequant_reduce_requant(codes_list, scales_list, bits_in: int, numel: int, bl
     when ``bits_out == 0``."""
     codes = np.stack([np.ascontiguousarray(c, dtype=np.uint8) for c in codes_list])
     scales = np.stack([np.ascontiguousarray(s, dtype=np.float32) for s in scales_list])
+    if block > 0:
+        _need(codes.shape[1], codes_nbytes(numel, bits_in), "each input's codes")
+        _need(scales.shape[1], numel // block, "each input's scales")
     total = np.empty(numel, dtype=np.float32)
     co = so = None
     if bits_out:
@@ -167,6 +182,9 @@ def dequant_average(codes_list, scales_list, bits: int, numel: int, block: int, 
     that contributed), one correctly rounded division per element."""
     codes = np.stack([np.ascontiguousarray(c, dtype=np.uint8) for c in codes_list])
     scales = np.stack([np.ascontiguousarray(s, dtype=np.float32) for s in scales_list])
+    if block > 0:
+        _need(codes.shape[1], codes_nbytes(numel, bits), "each input's codes")
+        _need(scales.shape[1], numel // block, "each input's scales")
     out = np.empty(numel, dtype=np.float32)
     rc = lib().oracle_dequant_average(_ptr(codes), codes.shape[1], _ptr(scales), scales.shape[1],
                                       len(codes_list), bits, numel, block, divisor, _ptr(out))
