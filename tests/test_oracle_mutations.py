@@ -4,7 +4,9 @@ Each case below plants one plausible slip in a scratch copy of the C oracle
 (``oracle/zpp_oracle.c``): a wrong Q, the nibble order, the rounding rule, a
 fused multiply-add or a reversed order in the hop sum, a transposed reorder,
 a reciprocal in place of a division, a missing absolute value, bf16
-truncation, unsigned nibbles, an average over the wrong count. The copy is
+truncation or ties away from zero, a bf16 decode one bit off, unsigned
+nibbles, a missing negative clamp, the inverse scale stored, a hop sum
+started from -0, an average over the wrong count. The copy is
 built and the oracle's pin tests run against it, in a process of their own;
 every mutant must make at least one of them fail. This checks the pins, not
 the oracle: it shows that none of these mistakes could hide in the oracle
@@ -46,6 +48,12 @@ MUTANTS = [
      "acc = fmaf((float)code_load(c, bits, i), s[i / block], acc);"),
     ("hop sum averaged over its inputs", "sum[i] = acc;", "sum[i] = acc / (float)n_inputs;"),
     ("average over the input count", "const float d = (float)divisor;", "const float d = (float)n_inputs;"),
+    ("hop sum started from -0", "float acc = 0.0f;", "float acc = -0.0f;"),
+    ("negative quotients not clamped", "if (r < (float)-Q)\n                r = (float)-Q;",
+     "if (0)\n                r = (float)-Q;"),
+    ("bf16 decoded one bit low", "uint32_t u = (uint32_t)h << 16;", "uint32_t u = (uint32_t)h << 15;"),
+    ("bf16 ties rounded away from zero", "u += 0x7fffu + keep_lsb;", "u += 0x8000u + 0u * keep_lsb;"),
+    ("inverse scale stored", "*scale_out = s;", "*scale_out = 1.0f / s;"),
 ]
 
 

@@ -110,6 +110,8 @@ def test_golden_reduce(oracle_lib, case):
     co, so, total = oracle.dequant_reduce_requant(codes, scales, case["bits_in"], n, case["block"],
                                                   case["bits_out"])
     assert total.tolist() == case["sum"]
+    if "sum_bits_hex" in case:  # == cannot tell -0 from +0: compare the bit patterns
+        assert [f"{v:08x}" for v in total.view(np.uint32).tolist()] == case["sum_bits_hex"]
     assert so.tolist() == case["out_scales"]
     assert _codes_int(co, case["bits_out"], n).tolist() == case["out_codes"]
 
