@@ -154,7 +154,7 @@ int64_t code_bytes(int64_t numel, int32_t bits) { return numel * bits / 8; }
 
 extern "C" {
 
-zpp_status zpp_quantize_blocks(const void *x, zpp_dtype x_dtype, int64_t numel, int32_t block, int32_t bits,
+zpp_status zpp_quantize_blocks(const void *x, int32_t x_dtype, int64_t numel, int32_t block, int32_t bits,
                                void *codes, float *scales, void *stream) {
     if (x_dtype != ZPP_BF16 && x_dtype != ZPP_FP32) return ZPP_ERR_ARG;
     if (bits != 8 && bits != 4) return ZPP_ERR_ARG;
@@ -173,7 +173,7 @@ zpp_status zpp_quantize_blocks(const void *x, zpp_dtype x_dtype, int64_t numel, 
     });
 }
 
-zpp_status zpp_quantize_reordered(const void *x, zpp_dtype x_dtype, int64_t slice_elems, int32_t n_nodes,
+zpp_status zpp_quantize_reordered(const void *x, int32_t x_dtype, int64_t slice_elems, int32_t n_nodes,
                                   int32_t gpus_per_node, int32_t first_slice, int32_t n_slices, int32_t block,
                                   int32_t bits, void *codes, float *scales, void *stream) {
     if (x_dtype != ZPP_BF16 && x_dtype != ZPP_FP32) return ZPP_ERR_ARG;
@@ -200,7 +200,7 @@ zpp_status zpp_quantize_reordered(const void *x, zpp_dtype x_dtype, int64_t slic
 }
 
 zpp_status zpp_dequantize_blocks(const void *codes, const float *scales, int32_t bits, int64_t numel, int32_t block,
-                                 void *y, zpp_dtype y_dtype, void *stream) {
+                                 void *y, int32_t y_dtype, void *stream) {
     if (y_dtype != ZPP_BF16 && y_dtype != ZPP_FP32) return ZPP_ERR_ARG;
     if (bits != 8 && bits != 4) return ZPP_ERR_ARG;
     if (!is_pow2_block(block) || numel < 0 || numel > ZPP_MAX_NUMEL || numel % block != 0) return ZPP_ERR_ARG;
@@ -297,7 +297,7 @@ zpp_status zpp_dequant_reduce_average(const void *codes_in, int64_t codes_stride
     });
 }
 
-const char *zpp_status_string(zpp_status status) {
+const char *zpp_status_string(int32_t status) {
     switch (status) {
     case ZPP_OK: return "ZPP_OK";
     case ZPP_ERR_NULL: return "ZPP_ERR_NULL: a required pointer is NULL";

@@ -100,6 +100,10 @@ typedef enum zpp_dtype {
     ZPP_FP32 = 2  /* IEEE-754 binary32 */
 } zpp_dtype;
 
+/* Element types and status codes cross the ABI as int32_t parameters (one of
+ * the enumerators above), so that any value a caller passes is well defined
+ * and is refused (ZPP_ERR_ARG, or "unknown zpp_status"). */
+
 /*
  * Block-quantize `numel` elements of `x` to `bits`-bit codes and per-block
  * scales. [QWZ] (8-bit weights before the forward all-gather) and [QGZ]
@@ -115,7 +119,7 @@ typedef enum zpp_dtype {
  * Non-finite inputs are outside the contract (they cannot fault the GPU,
  * but their codes are unspecified).
  */
-zpp_status zpp_quantize_blocks(const void *x, zpp_dtype x_dtype, int64_t numel,
+zpp_status zpp_quantize_blocks(const void *x, int32_t x_dtype, int64_t numel,
                                int32_t block, int32_t bits, void *codes, float *scales,
                                void *stream);
 
@@ -140,7 +144,7 @@ zpp_status zpp_quantize_blocks(const void *x, zpp_dtype x_dtype, int64_t numel,
  *   scales          out  n_slices * slice_elems / block floats, 4-B aligned
  *   stream          in   hipStream_t
  */
-zpp_status zpp_quantize_reordered(const void *x, zpp_dtype x_dtype, int64_t slice_elems, int32_t n_nodes,
+zpp_status zpp_quantize_reordered(const void *x, int32_t x_dtype, int64_t slice_elems, int32_t n_nodes,
                                   int32_t gpus_per_node, int32_t first_slice, int32_t n_slices, int32_t block,
                                   int32_t bits, void *codes, float *scales, void *stream);
 
@@ -158,7 +162,7 @@ zpp_status zpp_quantize_reordered(const void *x, zpp_dtype x_dtype, int64_t slic
  *   stream   in   hipStream_t
  */
 zpp_status zpp_dequantize_blocks(const void *codes, const float *scales, int32_t bits,
-                                 int64_t numel, int32_t block, void *y, zpp_dtype y_dtype,
+                                 int64_t numel, int32_t block, void *y, int32_t y_dtype,
                                  void *stream);
 
 /*
@@ -232,8 +236,9 @@ zpp_status zpp_dequant_reduce_average(const void *codes_in, int64_t codes_stride
                                       int32_t n_inputs, int32_t bits_in, int64_t numel,
                                       int32_t block, int32_t divisor, float *avg_out, void *stream);
 
-/* Static, human-readable name of a status code. Never NULL. */
-const char *zpp_status_string(zpp_status status);
+/* Static, human-readable name of a status code (a zpp_status value); any
+ * other value gives "unknown zpp_status". Never NULL. */
+const char *zpp_status_string(int32_t status);
 
 /* ZPP_ABI_VERSION of the loaded library. */
 int32_t zpp_abi_version(void);
