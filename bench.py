@@ -29,8 +29,9 @@ longest row is reported against the HBM roofline. Timed after the steps and
 reported beside them: the unfused pair (standalone reorder of the bf16
 bucket, then quantize of the reordered buffer), the other unfused order
 (quantize the bucket as it is, then reorder its codes and scales), and hop 2
-writing the averaged shard, and a plain 1 GiB device copy (the slice reorder
-with one slice) that each row is also compared with (`copy_frac`). The CPU baseline runs the plain C oracle (single thread) over
+writing the averaged shard, a plain 1 GiB device copy (the slice reorder
+with one slice) that each row is also compared with (`copy_frac`), and the
+step captured into a HIP graph and replayed (`graph_step`). The CPU baseline runs the plain C oracle (single thread) over
 the same work as one step (the reorder and the quantize as two oracle steps),
 twice.
 
@@ -282,6 +283,31 @@ def time_rows(torch, stream, fns, table, K):
         out[name] = {"ms": round(ms, 5),
                      "hbm_frac": round((rin + wout) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
     return out
+
+
+def graph_step_ms(torch, fns, K):
+    """Milliseconds per step when the step's launches are captured into one HIP
+    graph and the graph is replayed K times back to back."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # one eager pass on the capture stream first
+        for f in fns:
+            f()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for f in fns:
+            f()
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        graph.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / K
+    del graph
+    return ms
 
 
 def copy_ceiling(torch, z, stream, K):
@@ -611,6 +637,10 @@ def main() -> int:
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / K
 
+    # the same step captured once into a HIP graph and replayed K times (a
+    # caller that replays a fixed sequence pays no per-launch host work)
+    graph_ms = graph_step_ms(torch, fns, K)
+
     # the same K steps again with HIP events around every kernel row
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fns]
           for _ in range(K)]
@@ -692,6 +722,9 @@ def main() -> int:
                            "copy_frac": round((p[2] + p[3]) / (p[5] * 1e-3) / 1e9 / copy["GBps"], 4)}
                     for p in per},
         "copy_ceiling": copy,
+        "graph_step": {"ms_per_step": round(graph_ms, 4),
+                       "value": round(total_in / (graph_ms * 1e-3) / 1e9, 2),
+                       "what": "the same step captured once into a HIP graph, replayed K times"},
         "unfused_reorder_then_quantize": unfused,
         "beside_the_step": extra,
         "roofline": roofline,

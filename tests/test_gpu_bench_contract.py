@@ -48,6 +48,8 @@ def test_bench_prints_one_contract_line():
     assert rf["kernel"] in rows
     assert rows[rf["kernel"]]["ms"] == max(v["ms"] for v in rows.values())
 
+    assert d["graph_step"]["ms_per_step"] > 0 and d["graph_step"]["value"] > 0
+
     cp = d["copy_ceiling"]
     assert cp["bytes"] == 2 << 30 and cp["GBps"] > 0
     for name, v in rows.items():
