@@ -66,7 +66,8 @@ def test_abi_version_and_status_strings(z):
     assert z.zpp_abi_version() == 1
     for s in range(0, 8):
         assert z.zpp_status_string(s).startswith("ZPP_")
-    assert z.zpp_status_string(99) == "unknown zpp_status"
+    for bad in (99, -1, 8, -(1 << 31), (1 << 31) - 1):
+        assert z.zpp_status_string(bad) == "unknown zpp_status"
 
 
 # Fake device addresses: never dereferenced, because each case fails in the
@@ -78,6 +79,8 @@ def test_quantize_argument_errors(z):
     L = z.library()
     q = L.zpp_quantize_blocks
     assert q(A, 3, 256, 256, 8, A + 4096, A + 8192, None) == z.ZPP_ERR_ARG          # dtype
+    for bad in (0, -1, -(1 << 31), (1 << 31) - 1):
+        assert q(A, bad, 256, 256, 8, A + 4096, A + 8192, None) == z.ZPP_ERR_ARG
     assert q(A, 1, 256, 256, 6, A + 4096, A + 8192, None) == z.ZPP_ERR_ARG          # bits
     assert q(A, 1, 256, 100, 8, A + 4096, A + 8192, None) == z.ZPP_ERR_ARG          # block not pow2
     assert q(A, 1, 256, 16, 8, A + 4096, A + 8192, None) == z.ZPP_ERR_ARG           # block < 32
@@ -123,6 +126,8 @@ def test_quantize_reordered_argument_errors(z):
 def test_dequantize_argument_errors(z):
     d = z.library().zpp_dequantize_blocks
     assert d(A, A + 4096, 8, 256, 256, A + 8192, 0, None) == z.ZPP_ERR_ARG          # dtype
+    for bad in (-1, 3, -(1 << 31), (1 << 31) - 1):
+        assert d(A, A + 4096, 8, 256, 256, A + 8192, bad, None) == z.ZPP_ERR_ARG
     assert d(A, A + 4096, 5, 256, 256, A + 8192, 1, None) == z.ZPP_ERR_ARG          # bits
     assert d(A, A + 4096, 8, 257, 256, A + 8192, 1, None) == z.ZPP_ERR_ARG
     assert d(A, None, 8, 256, 256, A + 8192, 1, None) == z.ZPP_ERR_NULL
