@@ -137,6 +137,15 @@ def _free():
     torch.cuda.empty_cache()
 
 
+def _need_device_bytes(n: int) -> None:
+    """These tests hold tens of GiB at once; a device with less free memory
+    skips them (with the figures) rather than failing the whole run."""
+    _free()
+    free, total = torch.cuda.mem_get_info()
+    if free < n:
+        pytest.skip(f"needs {n / 2**30:.0f} GiB of device memory, {free / 2**30:.0f} of {total / 2**30:.0f} GiB free")
+
+
 def _rows_by_copies(t, width: int, idx: np.ndarray) -> np.ndarray:
     """Rows idx of t viewed as [-1, width], read back with plain slice copies
     (runs of consecutive rows at a time). torch's index gather kernel faulted
@@ -167,6 +176,7 @@ def test_dequantize_past_the_largest_grid():
     n = (1 << 35) + 5 * block                       # one-pass grid covers GRID_WAVES * 512 elements
     first_second_pass = GRID_WAVES * 512
     assert first_second_pass < n
+    _need_device_bytes(n * 3 + (n // block) * 16 + (1 << 30))     # codes, bf16 out, scales and temporaries
     print(f"dequantize int8 -> bf16, {n} elements (tile {first_second_pass} starts the second pass)", flush=True)
     gen = torch.Generator(device="cuda").manual_seed(41)
     codes = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda", generator=gen)
@@ -191,6 +201,7 @@ def test_quantize_past_the_largest_grid():
     n = (1 << 36) + 3 * 1024                        # one-pass grid covers GRID_WAVES * 1024 elements
     first_second_pass = GRID_WAVES * 1024
     assert first_second_pass < n
+    _need_device_bytes(n * 2 + n // 2 + (n // block) * 4 + (1 << 30))   # bf16 in, int4 codes, scales
     print(f"quantize bf16 -> int4, {n} elements (tile {first_second_pass} starts the second pass)", flush=True)
     gen = torch.Generator(device="cuda").manual_seed(47)
     x = torch.empty(n, dtype=torch.bfloat16, device="cuda")
