@@ -47,6 +47,11 @@
  *   - ranks are node-major (rank = node * gpus_per_node + local); hop 1 sends
  *     contiguous chunk j of every buffer to local rank j; hop 2 sends
  *     contiguous sub-chunk k of that chunk to node k.
+ *
+ * Every routine below is pinned by CPU tests that do not reuse this code:
+ * worked examples derived by hand, exact rational checks of each rounding,
+ * invariants, a NumPy re-derivation, and a brute-forced two-hop simulation.
+ * None is left "parity unpinned".
  */
 #include <math.h>
 #include <stdint.h>
