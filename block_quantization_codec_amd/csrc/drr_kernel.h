@@ -81,6 +81,11 @@ namespace {
 #ifndef ZPP_DRR_WIDE_E
 #define ZPP_DRR_WIDE_E 32
 #endif
+// 1: with 4-bit inputs the wide layout moves each input's codes into LDS
+// with loads that hold no registers (see consume_lds).
+#ifndef ZPP_DRR_LDS
+#define ZPP_DRR_LDS 1
+#endif
 // Below this many waves of the wide layout, lanes take 8 elements each so
 // that small outputs still spread over every SIMD.
 #ifndef ZPP_DRR_NARROW_WAVES
@@ -360,12 +365,125 @@ __device__ __forceinline__ void consume_overlapped(const uint8_t *__restrict__ c
     }
 }
 
+// ---- the wide layout with codes staged through LDS -------------------------
+//
+// With 4-bit inputs a lane's codes of one input are one 16-byte vector. The
+// batch's scales are loaded into registers as elsewhere; each code vector
+// then goes straight from memory into this wave's own LDS slot
+// (global_load_lds_dwordx4: a kilobyte per instruction, no registers held
+// while it is in flight), and is read back just before it is summed. The
+// registers saved let 5 waves share a SIMD instead of 4 (the kernel is held
+// to that register budget), which keeps more loads in flight while other
+// waves sum and requantize.
+
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding. The compiler does not track loads into LDS, so their readers
+// wait here explicitly; the clobber keeps memory accesses on their side.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Sum inputs K .. NB-1 of a batch whose code vectors sit in LDS slots 0 ..
+// NB-1, in input order. The loads into the slots were issued in slot order
+// after every other outstanding load had completed, and vector-memory
+// operations complete in order, so slot K has arrived once at most NB-1-K
+// operations are outstanding. Positions from `valid` on are padding.
+template <typename G, int NB, int K = 0>
+__device__ __forceinline__ void sum_from_lds(const uint32_t (*slot)[kWave][4], const float (&s)[NB][G::U], int lane,
+                                             float (&acc)[G::U][G::E], bool first, int valid, bool fast) {
+    if constexpr (K < NB) {
+        if (K == 0 || K < valid) {
+            wait_vmem<NB - 1 - K>();
+            uint32_t w[1][G::U][G::ND];
+            float sk[1][G::U];
+#pragma unroll
+            for (int u = 0; u < G::U; ++u) {
+                const uint32_t *q = slot[K * G::U + u][lane];
+#pragma unroll
+                for (int d = 0; d < G::ND; ++d) w[0][u][d] = q[d];
+                sk[0][u] = s[K][u];
+            }
+            if (K == 0 && first) {
+                if (fast)
+                    accumulate<G, 1, true, true>(w, sk, acc, 1);
+                else
+                    accumulate<G, 1, true, false>(w, sk, acc, 1);
+            } else {
+                if (fast)
+                    accumulate<G, 1, false, true>(w, sk, acc, 1);
+                else
+                    accumulate<G, 1, false, false>(w, sk, acc, 1);
+            }
+        }
+        sum_from_lds<G, NB, K + 1>(slot, s, lane, acc, first, valid, fast);
+    }
+}
+
+// All n_inputs inputs in batches of NB through the wave's NB LDS slots; the
+// first batch starts the sums, and a last, partial batch loads its padding
+// from the last input and skips it (as consume_padded does).
+template <typename G, int NB>
+__device__ __forceinline__ void consume_lds(const uint8_t *__restrict__ codes_in, int64_t codes_stride,
+                                            const float *__restrict__ scales_in, int64_t scales_stride,
+                                            int n_inputs, const LaneOffsets<G> &o, float (&acc)[G::U][G::E],
+                                            uint32_t (*slot)[kWave][4], int lane) {
+    static_assert(G::U == 1 && G::ND == 4, "one 16-byte code vector per input and lane");
+    for (int r0 = 0; r0 < n_inputs; r0 += NB) {
+        // the previous batch's reads of the slots are complete before they are refilled
+        if (r0 > 0) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        float s[NB][G::U];
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            const int ri = min(r0 + k, n_inputs - 1);
+            const uint8_t *sc = reinterpret_cast<const uint8_t *>(scales_in + static_cast<int64_t>(ri) * scales_stride);
+#pragma unroll
+            for (int u = 0; u < G::U; ++u) s[k][u] = *reinterpret_cast<const float *>(sc + o.scale[u]);
+        }
+        // The batch's choice of product formula (see add_batch). Taking it
+        // here makes the compiler wait for the scales before the loads into
+        // LDS are issued, so that only those are outstanding below.
+        uint32_t hi = 0u;
+#pragma unroll
+        for (int k = 0; k < NB; ++k)
+#pragma unroll
+            for (int u = 0; u < G::U; ++u) hi = max(hi, as_u(s[k][u]) << 1);
+        const bool fast = hi <= (as_u(0x1p103f) << 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            const int ri = min(r0 + k, n_inputs - 1);
+            const uint8_t *c = codes_in + static_cast<int64_t>(ri) * codes_stride;
+#pragma unroll
+            for (int u = 0; u < G::U; ++u)
+                __builtin_amdgcn_global_load_lds(static_cast<const void *>(c + o.code[u]),
+                                                 (__attribute__((address_space(3))) void *)(&slot[k * G::U + u][0][0]),
+                                                 16, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        sum_from_lds<G, NB>(slot, s, lane, acc, r0 == 0, n_inputs - r0, fast);
+    }
+    wait_vmem<0>();  // padding loads too: none may land in LDS after this wave moves on
+}
+
 // Elements one launch covers at most; a multiple of every block size and
 // tile, small enough that every lane offset fits in 32 bits.
 constexpr int64_t kDrrChunk = INT64_C(1) << 29;
 
+// Minimum waves per SIMD a hop kernel is compiled for: 5 for the LDS-staged
+// wide layout, whose registers fit that budget (and whose 32 KB of LDS per
+// workgroup allow 5 workgroups per CU); no minimum for the other layouts.
+template <int BITS_IN, int LOG2B, int E>
+constexpr int drr_min_waves() {
+    return ZPP_DRR_LDS && DrrGeom<BITS_IN, 0, LOG2B, E>::U == 1 && DrrGeom<BITS_IN, 0, LOG2B, E>::ND == 4 &&
+                   !DrrGeom<BITS_IN, 0, LOG2B, E>::OVERLAP
+               ? 5
+               : 1;
+}
+
 template <int BITS_IN, int BITS_OUT, int LOG2B, int E, bool AVG>
-__global__ __launch_bounds__(kBlockThreads) void drr_kernel(const uint8_t *__restrict__ codes_in,
+__global__ __launch_bounds__(kBlockThreads)
+__attribute__((amdgpu_waves_per_eu(drr_min_waves<BITS_IN, LOG2B, E>(), 8))) void drr_kernel(const uint8_t *__restrict__ codes_in,
                                                             int64_t codes_stride,
                                                             const float *__restrict__ scales_in,
                                                             int64_t scales_stride, int n_inputs, int numel,
@@ -412,6 +530,10 @@ __global__ __launch_bounds__(kBlockThreads) void drr_kernel(const uint8_t *__res
             consume_overlapped<G, G::RB>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, o, r, acc);
             if constexpr (G::RB > 4) consume<G, 4>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, o, r, acc);
             consume<G, 1>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, o, r, acc);
+        } else if constexpr (ZPP_DRR_LDS && G::U == 1 && G::ND == 4) {
+            __shared__ uint32_t lds_codes[kBlockThreads / kWave][G::RB][kWave][4];  // 8 KB per wave
+            consume_lds<G, G::RB>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, o, acc,
+                                  lds_codes[threadIdx.x / kWave], lane);
         } else {
             consume_padded<G, G::RB>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, o, acc);
         }
