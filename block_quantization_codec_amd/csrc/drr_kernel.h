@@ -610,8 +610,16 @@ template <int BITS_IN, int BITS_OUT, int LOG2B, bool AVG>
 hipError_t launch(const DrrArgs &a) {
     using Wide = DrrGeom<BITS_IN, BITS_OUT, LOG2B, ZPP_DRR_WIDE_E>;
     const int64_t wide_waves = (a.numel + Wide::TILE - 1) / Wide::TILE;
-    if (wide_waves >= ZPP_DRR_NARROW_WAVES) return launch_e<BITS_IN, BITS_OUT, LOG2B, ZPP_DRR_WIDE_E, AVG>(a);
-    return launch_e<BITS_IN, BITS_OUT, LOG2B, 8, AVG>(a);
+    // Blocks of 4096 elements span 8 narrow segments per tile, whose codes
+    // and sums do not fit the registers (hundreds of bytes of spills with
+    // 8-bit inputs): they always take the wide layout, 2 segments per tile,
+    // which measured faster at every size.
+    if constexpr (LOG2B >= 12) {
+        return launch_e<BITS_IN, BITS_OUT, LOG2B, ZPP_DRR_WIDE_E, AVG>(a);
+    } else {
+        if (wide_waves >= ZPP_DRR_NARROW_WAVES) return launch_e<BITS_IN, BITS_OUT, LOG2B, ZPP_DRR_WIDE_E, AVG>(a);
+        return launch_e<BITS_IN, BITS_OUT, LOG2B, 8, AVG>(a);
+    }
 }
 
 template <int BITS_IN, int BITS_OUT, bool AVG>
