@@ -25,8 +25,10 @@
 // for small outputs, which then still spread over every SIMD. Inputs are
 // read a batch at a time, all loads of a batch in flight before the batch is
 // summed in input order. With E = 32 every batch holds 8 inputs (a last,
-// partial one skips its padding); with E = 8 the next batch's loads are also
-// issued before the current batch is summed. The requantized block maximum
+// partial one skips its padding), and 4-bit code vectors land in the wave's
+// own LDS slots rather than in registers (see consume_lds); with E = 8 the
+// next batch's loads are also issued before the current batch is summed.
+// Blocks of 4096 elements always take E = 32. The requantized block maximum
 // is reduced across the block's lanes with DPP / permlane swaps.
 #pragma once
 
