@@ -185,14 +185,17 @@ def test_empty_is_a_no_op():
 @pytest.mark.parametrize("bits_in,bits_out,R,block", [(4, 4, 8, 256), (8, 8, 3, 256), (4, 0, 5, 256),
                                                        (8, 4, 9, 256), (4, 8, 17, 256), (8, 0, 16, 256),
                                                        (4, 4, 8, 32), (8, 8, 5, 32), (4, 4, 8, 4096),
-                                                       (8, 0, 3, 4096)])
+                                                       (8, 0, 3, 4096), (4, 4, 16, 256), (4, 0, 9, 128),
+                                                       (4, 4, 1, 512)])
 def test_wide_lane_path(bits_in, bits_out, R, block):
     """Outputs large enough for the 32-elements-per-lane layout (at least 4096 waves of
     2048 elements), with a ragged tail; the small cases above use 8 elements per lane.
     That layout sums batches of 8 inputs: fewer than 8, 9 and 17 inputs end in a
-    partial batch, 8 and 16 do not; mixed code widths use their own kernels. Block 32
-    gives each lane a block of its own (no cross-lane maximum); block 4096 spans two
-    2048-element segments per tile."""
+    partial batch, 8 and 16 do not; mixed code widths use their own kernels. With
+    4-bit inputs and blocks up to 2048 the code vectors land in LDS slots: 16 inputs
+    refill the slots once, 9 leave one live input in the second batch, 1 is a single
+    input. Block 32 gives each lane a block of its own (no cross-lane maximum); block
+    4096 spans two 2048-element segments per tile."""
     numel = 8192 * 2048 + (3 * 2048 + 5 * block if block < 2048 else 3 * block)   # a multiple of the block
     rng = np.random.default_rng([R, bits_in])
     per_c = numel * bits_in // 8
