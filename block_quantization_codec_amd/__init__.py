@@ -30,9 +30,9 @@ ZPP_ERR_NULL = 1
 ZPP_ERR_ARG = 2
 ZPP_ERR_ALIGN = 3
 ZPP_ERR_UNSUPPORTED = 4
-ZPP_ERR_OVERLAP = 5
-ZPP_ERR_POINTER = 6
-ZPP_ERR_LAUNCH = 7
+ZPP_ERR_LAUNCH = 5
+ZPP_ERR_OVERLAP = 6
+ZPP_ERR_POINTER = 7
 
 ZPP_BF16 = 1
 ZPP_FP32 = 2

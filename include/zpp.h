@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define ZPP_ABI_VERSION 1
+#define ZPP_ABI_VERSION 2
 #define ZPP_MIN_BLOCK 32
 #define ZPP_MAX_BLOCK 4096
 #define ZPP_MAX_INPUTS 4096
@@ -90,9 +90,12 @@ typedef enum zpp_status {
     ZPP_ERR_ARG = 2,         /* size, block, bit width, count or stride invalid   */
     ZPP_ERR_ALIGN = 3,       /* pointer or stride not aligned as required         */
     ZPP_ERR_UNSUPPORTED = 4, /* valid request the library does not implement      */
-    ZPP_ERR_OVERLAP = 5,     /* an output overlaps an input or another output     */
-    ZPP_ERR_POINTER = 6,     /* a pointer is not memory the GPU can address       */
-    ZPP_ERR_LAUNCH = 7       /* the HIP runtime reported an error for the launch  */
+    ZPP_ERR_LAUNCH = 5,      /* the HIP runtime reported an error for the launch  */
+    /* Beyond the five error kinds above, the library tells apart two more
+     * argument errors; they come after ZPP_ERR_LAUNCH so that codes 0-5
+     * keep their meaning for callers that know only those. */
+    ZPP_ERR_OVERLAP = 6,     /* an output overlaps an input or another output     */
+    ZPP_ERR_POINTER = 7      /* a pointer is not memory the GPU can address       */
 } zpp_status;
 
 typedef enum zpp_dtype {

@@ -63,11 +63,24 @@ def test_library_exports_every_declared_symbol(z):
 
 
 def test_abi_version_and_status_strings(z):
-    assert z.zpp_abi_version() == 1
+    assert z.zpp_abi_version() == 2
     for s in range(0, 8):
         assert z.zpp_status_string(s).startswith("ZPP_")
     for bad in (99, -1, 8, -(1 << 31), (1 << 31) - 1):
         assert z.zpp_status_string(bad) == "unknown zpp_status"
+
+
+def test_status_values_match_the_header(z):
+    """The numeric status codes: 0-5 as the boundary contract fixes them
+    (OK, NULL, ARG, ALIGN, UNSUPPORTED, LAUNCH), the two extra argument
+    errors after them; the binding, the header and the library agree."""
+    want = {"ZPP_OK": 0, "ZPP_ERR_NULL": 1, "ZPP_ERR_ARG": 2, "ZPP_ERR_ALIGN": 3, "ZPP_ERR_UNSUPPORTED": 4,
+            "ZPP_ERR_LAUNCH": 5, "ZPP_ERR_OVERLAP": 6, "ZPP_ERR_POINTER": 7}
+    hdr = open(HEADER).read()
+    for name, v in want.items():
+        assert getattr(z, name) == v, name
+        assert re.search(rf"\b{name} = {v}\b", hdr), name
+        assert z.zpp_status_string(v).startswith(name), (name, z.zpp_status_string(v))
 
 
 # Fake device addresses: never dereferenced, because each case fails in the

@@ -1,13 +1,15 @@
 """GPU parity at the full workload sizes, in the launch shapes the benchmark uses.
 
-Where the oracle can run on everything in seconds (the 4096x4096 weight, the
-8-rank 2x4 chain, the 64-shard layer) the comparison is complete; for the
-500M-element bucket and the 855M-element GQA layer it covers the first and
-last blocks plus thousands of randomly sampled blocks (blocks are
-independent, so the oracle recomputes exactly those), and asserts
-size-independent properties (code range, error bound) on whole outputs.
-Inputs come from the seeded generators; inputs the oracle needs in quantized
-form (peer contributions) are quantized by the oracle, never by the GPU.
+Every output of every workload is compared with the oracle, bit for bit: the
+4096x4096 weight, the 8-rank 2x4 chain, the 64-shard layer, the 500M-element
+bucket at 32x8 (reorder, unfused and fused int4 quantize, the whole hop-1
+chunk, the hop-2 slice and its average) and the 855M-element GQA layer
+(int8 codes, scales and bf16 round trip of the weight; int4 codes, scales
+and binary32 round trip of the gradient). At the two largest sizes the
+oracle runs over independent block ranges on a thread pool
+(tests/oracle_par.py), which gives the same bytes as one call. Inputs come
+from the seeded generators; inputs the oracle needs in quantized form (peer
+contributions) are quantized by the oracle, never by the GPU.
 """
 from __future__ import annotations
 
@@ -17,6 +19,7 @@ import numpy as np
 import pytest
 
 import oracle
+import oracle_par
 import synth
 from gpu_util import assert_bits_equal, assert_within_scale, dev, host, need_gpu, torch
 
@@ -36,28 +39,6 @@ def _z():
 def _say(msg):
     print(msg, flush=True)
     sys.stdout.flush()
-
-
-def _sample(nblocks: int, k: int, seed: int) -> np.ndarray:
-    rng = np.random.default_rng(seed)
-    idx = np.concatenate([np.arange(min(64, nblocks)), np.arange(max(0, nblocks - 64), nblocks),
-                          rng.choice(nblocks, min(k, nblocks), replace=False)])
-    return np.unique(idx)
-
-
-def _rows(a, width: int, idx: np.ndarray) -> np.ndarray:
-    """Rows `idx` of a flat array viewed as [-1, width] (numpy or device tensor)."""
-    if isinstance(a, np.ndarray):
-        return a.reshape(-1, width)[idx].reshape(-1)
-    t = a.reshape(-1, width)[torch.from_numpy(idx).to(a.device)]
-    return host(t).reshape(-1)
-
-
-def _codes_q(codes: np.ndarray, bits: int) -> np.ndarray:
-    if bits == 8:
-        return codes.view(np.int8)
-    q = np.stack([(codes & 0xF).astype(np.int8), (codes >> 4).astype(np.int8)], 1).reshape(-1)
-    return np.where(q >= 8, q - 16, q).astype(np.int8)
 
 
 # --------------------------------------------------------------------------
@@ -173,7 +154,7 @@ def test_qwz_dequant_64_shards():
 
 
 # --------------------------------------------------------------------------
-# qgZ 32 nodes x 8 GPUs, one GPU's 500M-element bucket (rank 255), sampled
+# qgZ 32 nodes x 8 GPUs, one GPU's 500M-element bucket (rank 255), complete
 # --------------------------------------------------------------------------
 
 def test_qgz_int4_32x8_rank255_chain():
@@ -233,28 +214,23 @@ def test_qgz_int4_32x8_rank255_chain():
 
     _say("compare reorder (complete)")
     assert_bits_equal(host(reord), o_re, "reorder")
-    _say("compare quantize (sampled)")
-    idx = _sample(P // B, 4000, 1)
-    oc, os_ = oracle.quantize(_rows(o_re, B, idx), B, 4)
-    assert_bits_equal(_rows(codes, B // 2, idx), oc, "codes (sampled)")
-    assert_bits_equal(_rows(scales, 1, idx), os_, "scales (sampled)")
-    assert_bits_equal(host(codes[local * C // 2:(local + 1) * C // 2]), oq_own[0], "own chunk codes")
-    assert_bits_equal(_rows(fc, B // 2, idx), oc, "fused reorder+quantize codes (sampled)")
-    assert_bits_equal(_rows(fs, 1, idx), os_, "fused reorder+quantize scales (sampled)")
-    assert_bits_equal(host(fc[local * C // 2:]), oq_own[0], "fused own chunk codes")
-    assert_bits_equal(host(fs[local * C // B:]), oq_own[1], "fused own chunk scales")
-    _say("compare hop 1 (sampled + own sub-chunk)")
+    del reord
+    _say("compare quantize, unfused and fused (complete)")
+    oc, os_ = oracle_par.quantize(o_re, B, 4)
+    assert_bits_equal(oc[local * C // 2:(local + 1) * C // 2], oq_own[0], "oracle own chunk, two ways")
+    assert_bits_equal(host(codes), oc, "codes")
+    assert_bits_equal(host(scales), os_, "scales")
+    assert_bits_equal(host(fc), oc, "fused reorder+quantize codes")
+    assert_bits_equal(host(fs), os_, "fused reorder+quantize scales")
+    del oc, os_
+    _say("compare hop 1 (complete)")
     ins_c = [q[0] for q in oq_peers] + [oq_own[0]]
     ins_s = [q[1] for q in oq_peers] + [oq_own[1]]
-    idx1 = np.unique(np.concatenate([_sample(C // B, 3000, 2),
-                                     np.arange(node * S // B, (node + 1) * S // B)]))
-    co, so, _ = oracle.dequant_reduce_requant([_rows(cc, B // 2, idx1) for cc in ins_c],
-                                              [_rows(ss, 1, idx1) for ss in ins_s], 4, idx1.size * B, B, 4)
-    assert_bits_equal(_rows(h1c, B // 2, idx1), co, "hop-1 codes")
-    assert_bits_equal(_rows(h1s, 1, idx1), so, "hop-1 scales")
+    co, so, _ = oracle_par.dequant_reduce_requant(ins_c, ins_s, 4, C, B, 4)
+    assert_bits_equal(host(h1c), co, "hop-1 codes")
+    assert_bits_equal(host(h1s), so, "hop-1 scales")
     _say("compare hop 2 (complete slice)")
-    own_sub = (_rows(co, B // 2, np.searchsorted(idx1, np.arange(node * S // B, (node + 1) * S // B))),
-               _rows(so, 1, np.searchsorted(idx1, np.arange(node * S // B, (node + 1) * S // B))))
+    own_sub = (co[node * S // 2:(node + 1) * S // 2], so[node * S // B:(node + 1) * S // B])
     o_fin = oracle.dequant_sum([q[0] for q in oq_parts] + [own_sub[0]], [q[1] for q in oq_parts] + [own_sub[1]],
                                4, S, B)
     fin = host(final)
@@ -269,7 +245,7 @@ def test_qgz_int4_32x8_rank255_chain():
 
 
 # --------------------------------------------------------------------------
-# 70B-scale GQA layer: int8 weight block 512, int4 gradient block 128, sampled
+# 70B-scale GQA layer: int8 weight block 512, int4 gradient block 128, complete
 # --------------------------------------------------------------------------
 
 def test_gqa_layer_mixed_codec():
@@ -277,22 +253,13 @@ def test_gqa_layer_mixed_codec():
     _say("generate GQA layer weight and gradient")
     W = synth.gqa_weight()
     G = synth.gqa_grad()
+    n = W.size
     wd, gd = dev(W), dev(G)
     wc, ws = z.quantize(wd, 512, 8)
-    wy = z.dequantize(wc, ws, 8, W.size, 512, dtype=torch.bfloat16)
+    wy = z.dequantize(wc, ws, 8, n, 512, dtype=torch.bfloat16)
     gc, gs = z.quantize(gd, 128, 4)
+    gy = z.dequantize(gc, gs, 4, n, 128, dtype=torch.float32)
     torch.cuda.synchronize()
-    _say("compare sampled blocks")
-    iw = _sample(W.size // 512, 4000, 3)
-    oc, os_ = oracle.quantize(_rows(W, 512, iw), 512, 8)
-    assert_bits_equal(_rows(wc, 512, iw), oc, "weight codes")
-    assert_bits_equal(_rows(ws, 1, iw), os_, "weight scales")
-    assert_bits_equal(_rows(wy.view(torch.int16), 512, iw).view(np.uint16),
-                      oracle.dequantize(oc, os_, 8, iw.size * 512, 512, out="bf16"), "weight bf16")
-    ig = _sample(G.size // 128, 4000, 4)
-    oc, os_ = oracle.quantize(_rows(G, 128, ig), 128, 4)
-    assert_bits_equal(_rows(gc, 64, ig), oc, "grad codes")
-    assert_bits_equal(_rows(gs, 1, ig), os_, "grad scales")
     _say("whole-output properties")
     # every int8 code in [-127, 127]; every block with a nonzero scale has a +-127 code
     q = wc.view(torch.int8)
@@ -303,3 +270,20 @@ def test_gqa_layer_mixed_codec():
     err = (wy.float() - wd.float()).abs().view(-1, 512)
     lim = ws.view(-1, 1) * (0.5 + 2.0 ** -15) + wy.float().abs().view(-1, 512) * 2.0 ** -8
     assert bool((err <= lim).all())
+    del q, amax, err, lim, wd, gd
+
+    _say("compare the weight's int8 codes, scales and bf16 round trip (complete)")
+    oc, os_ = oracle_par.quantize(W, 512, 8)
+    assert_bits_equal(host(ws), os_, "weight scales")
+    assert_bits_equal(host(wc), oc, "weight codes")
+    del wc
+    assert_bits_equal(host(wy), oracle_par.dequantize(oc, os_, 8, n, 512, out="bf16"), "weight bf16")
+    del wy, oc, os_, W
+    _say("compare the gradient's int4 codes, scales and binary32 round trip (complete)")
+    oc, os_ = oracle_par.quantize(G, 128, 4)
+    assert_bits_equal(host(gs), os_, "grad scales")
+    assert_bits_equal(host(gc), oc, "grad codes")
+    want = oracle_par.dequantize(oc, os_, 4, n, 128, out="f32")
+    got = host(gy)
+    assert_within_scale(got, want, np.repeat(os_, 128), "grad fp32 within 1e-5 s")
+    assert_bits_equal(got, want, "grad fp32 bits")
