@@ -10,8 +10,8 @@ One step is one pass of the whole per-GPU hot path on resident HBM inputs:
        reordered bucket into the send buffer, chunk 7 straight into its slot
        of the hop-1 receive buffer); the reordered bf16 bucket is never written
     3. hop 1: 8-way dequantize + fp32 sum + int4 requantize of the receive
-       buffer (sub-chunks 0-30 into the hop-2 send buffer, sub-chunk 31 into
-       its slot of the hop-2 receive buffer)
+       buffer in one launch (sub-chunks 0-30 into the hop-2 send buffer,
+       sub-chunk 31 into its slot of the hop-2 receive buffer)
     4. hop 2: 32-way dequantize + fp32 sum into the owned fp32 shard
   qwZ and qgZ on one 70B-scale GQA layer (hidden 8192, 64/8 heads, FFN 28672,
   855,638,016 weights), N(0, 0.01) with 0.01 % outliers x100:
@@ -31,9 +31,10 @@ bucket, then quantize of the reordered buffer), the other unfused order
 (quantize the bucket as it is, then reorder its codes and scales), and hop 2
 writing the averaged shard, a plain 1 GiB device copy (the slice reorder
 with one slice) that each row is also compared with (`copy_frac`), and the
-step captured into a HIP graph and replayed (`graph_step`). The CPU baseline runs the plain C oracle (single thread) over
-the same work as one step (the reorder and the quantize as two oracle steps),
-twice.
+step captured into a HIP graph and replayed (`graph_step`). The CPU baseline
+runs the plain C oracle over the same work as one step (the reorder and the
+quantize as two oracle steps), once on one core and twice on every core the
+process may use (independent block ranges on a thread pool).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --configs       (one JSON line: kernel times at the 4096x4096,
@@ -173,12 +174,14 @@ class Step:
              "quantize_kernel<4, 8, false>"),
             ("reorder_int4_codes_and_scales", "reorder", P // 2 + 4 * P // B, P // 2 + 4 * P // B,
              "reorder_kernel<16> + reorder_kernel<8>"),
+            ("hop1_two_launches_unsplit", "drr", g * (C // 2 + 4 * C // B), C // 2 + 4 * C // B,
+             "drr_kernel<4, 4, 8, 32> + drr_kernel<4, 4, 8, 8>"),
         ]
         self.kernels = [
             ("reorder_quantize_int4_b256", "quantize", 2 * P, P // 2 + 4 * P // B,
              "quantize_kernel<4, 8, false> x2"),
             ("hop1_drr_8way_int4_b256", "drr", g * (C // 2 + 4 * C // B), C // 2 + 4 * C // B,
-             "drr_kernel<4, 4, 8, 32> + drr_kernel<4, 4, 8, 8>"),
+             "drr_kernel<4, 4, 8, 32>"),
             ("hop2_reduce_32way_fp32", "drr", n * (S // 2 + 4 * S // B), 4 * S, "drr_kernel<4, 0, 8, 8>"),
             ("quantize_int8_b512_gqa_weight", "quantize", 2 * nw, nw + 4 * nw // 512,
              "quantize_kernel<8, 9, false>"),
@@ -205,11 +208,11 @@ class Step:
                                      self.recv1_c[loc * C // 2:], self.recv1_s[loc * C // B:])
 
         def hop1():
-            z.zpp_dequant_reduce_requant(self.recv1_c, C // 2, self.recv1_s, C // B, g, 4, node * S, B,
-                                         self.send2_c, self.send2_s, 4, None)
-            z.zpp_dequant_reduce_requant(self.recv1_c[node * S // 2:], C // 2, self.recv1_s[node * S // B:],
-                                         C // B, g, 4, S, B, self.recv2_c[node * S // 2:],
-                                         self.recv2_s[node * S // B:], 4, None)
+            # one pass: sub-chunk `node` (this GPU's own) straight into its slot of
+            # the hop-2 receive buffer, the other 31 into the hop-2 send buffer
+            z.zpp_dequant_reduce_requant_split(self.recv1_c, C // 2, self.recv1_s, C // B, g, 4, C, B, node * S, S,
+                                               self.send2_c, self.send2_s, self.recv2_c[node * S // 2:],
+                                               self.recv2_s[node * S // B:], 4)
 
         def hop2():
             z.zpp_dequant_reduce_requant(self.recv2_c, S // 2, self.recv2_s, S // B, n, 4, S, B, None, None, 0,
@@ -262,7 +265,18 @@ class Step:
             z.zpp_reorder_slices(self.pre_c, self.post_c, S // 2, n, g)
             z.zpp_reorder_slices(self.pre_s, self.post_s, 4 * S // B, n, g)
 
-        return [hop2_average, quantize_before_reorder, reorder_codes_and_scales]
+        def hop1_two_launches():
+            # hop 1 as two calls of the unsplit step: sub-chunks 0..node-1 to the
+            # send buffer, then sub-chunk `node` to its receive slot
+            node = self.node
+            C = c.chunk_len
+            z.zpp_dequant_reduce_requant(self.recv1_c, C // 2, self.recv1_s, C // B, g, 4, node * S, B,
+                                         self.send2_c, self.send2_s, 4, None)
+            z.zpp_dequant_reduce_requant(self.recv1_c[node * S // 2:], C // 2, self.recv1_s[node * S // B:],
+                                         C // B, g, 4, S, B, self.recv2_c[node * S // 2:],
+                                         self.recv2_s[node * S // B:], 4, None)
+
+        return [hop2_average, quantize_before_reorder, reorder_codes_and_scales, hop1_two_launches]
 
 
 def time_rows(torch, stream, fns, table, K):
@@ -334,9 +348,24 @@ def copy_ceiling(torch, z, stream, K):
             "bytes": 2 * n, "ms": round(ms, 5), "GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
 
 
-def cpu_baseline(step: "Step", frac: float = 1.0, passes: int = 2):
-    """The oracle, as it stands, on the first `frac` of every kernel's work,
-    `passes` times over (the host's single-thread oracle needs ~5-7 s a pass)."""
+def _block_ranges(nblocks: int, parts: int):
+    parts = max(1, min(parts, nblocks))
+    step = -(-nblocks // parts)
+    return [(b, min(nblocks, b + step)) for b in range(0, nblocks, step)]
+
+
+def cpu_baseline(step: "Step", passes_one: int = 1, passes_all: int = 2):
+    """The oracle, as it stands, over the same work as one step: once on one
+    core, then on every core this process may use. The all-cores leg runs the
+    unchanged oracle over independent pieces on a thread pool (ctypes releases
+    the GIL during each oracle call): block ranges for the quantizers, the
+    dequantizer and the hop reductions, and column ranges of the [slices]
+    [slice] view for the reorder (each slice's columns move as a whole).
+    Blocks and columns are independent, so the pieces are the same work. The
+    reorder and the quantize are separate oracle steps (the oracle has no
+    fused kernel)."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
 
     import oracle
@@ -344,59 +373,95 @@ def cpu_baseline(step: "Step", frac: float = 1.0, passes: int = 2):
     oracle.lib()
     c = step.c
     n, g, B = c.n_nodes, c.gpus_per_node, c.block
-    S = c.slice_len
-    sub_s = (int(S * frac) // B) * B           # a shorter slice, same slicing
+    N, S, Cl = n * g, c.slice_len, c.chunk_len
     nw = step.w_np.size
-    w_n = (int(nw * frac) // 512) * 512
-    g_n = (int(nw * frac) // 128) * 128
-    bucket = step.bucket_np.reshape(n * g, S)[:, :sub_s].reshape(-1)
-    hop_n = (int(c.chunk_len * frac) // B) * B
-    hop2_n = sub_s
-    hc, hs = oracle.quantize(bucket[:hop_n], B, 4)      # hop inputs (their values do not change the work)
-    hop_inputs_c = [hc] * g
-    hop_inputs_s = [hs] * g
-    h2c, h2s = oracle.quantize(bucket[:hop2_n], B, 4)
-    timings = []
+    bucket = step.bucket_np
+    hc, hs = oracle.quantize(bucket[:Cl], B, 4)       # hop inputs (their values do not change the work)
+    h2c, h2s = oracle.quantize(bucket[:S], B, 4)
+    w_q = oracle.quantize(step.w_np, 512, 8)
+    cores = len(os.sched_getaffinity(0))
+    PARTS = 4 * cores
+    # the reorder's pieces: column ranges of the [N][S] view, made contiguous beforehand
+    cols = [(c0, c1) for c0, c1 in _block_ranges(S // B, PARTS)]
+    re_pieces = [np.ascontiguousarray(bucket.reshape(N, S)[:, c0 * B:c1 * B]).reshape(-1) for c0, c1 in cols]
+    reordered = oracle.reorder_slices(bucket, n, g)
 
-    def timed(name, in_bytes, fn):
-        t = time.perf_counter()
-        out = fn()
-        timings.append((name, in_bytes, time.perf_counter() - t))
-        return out
+    def work(pool):
+        """(name, input bytes, callable) for every kernel row of one step."""
+        def par(fn, nblocks):
+            rs = _block_ranges(nblocks, PARTS if pool else 1)
+            if pool is None:
+                return lambda: [fn(*r) for r in rs]
+            return lambda: list(pool.map(lambda r: fn(*r), rs))
 
-    for _ in range(passes):
-        re_ = timed("reorder", bucket.nbytes, lambda: oracle.reorder_slices(bucket, n, g))
-        timed("quantize_int4_b256", re_.nbytes, lambda: oracle.quantize(re_, B, 4))
-        timed("hop1", g * (hop_n // 2 + 4 * hop_n // B),
-              lambda: oracle.dequant_reduce_requant(hop_inputs_c, hop_inputs_s, 4, hop_n, B, 4))
-        timed("hop2", n * (hop2_n // 2 + 4 * hop2_n // B),
-              lambda: oracle.dequant_reduce_requant([h2c] * n, [h2s] * n, 4, hop2_n, B, 0))
-        wq = timed("quantize_int8_b512", 2 * w_n, lambda: oracle.quantize(step.w_np[:w_n], 512, 8))
-        timed("dequantize_int8_b512", w_n + 4 * w_n // 512,
-              lambda: oracle.dequantize(wq[0], wq[1], 8, w_n, 512, out="bf16"))
-        timed("quantize_int4_b128", 2 * g_n, lambda: oracle.quantize(step.g_np[:g_n], 128, 4))
-    total_in = sum(t[1] for t in timings)
-    total_s = sum(t[2] for t in timings)
+        reorder = (lambda: oracle.reorder_slices(bucket, n, g)) if pool is None else \
+            (lambda: list(pool.map(lambda i: oracle.reorder_slices(re_pieces[i], n, g), range(len(re_pieces)))))
+        return [
+            ("reorder", bucket.nbytes, reorder),
+            ("quantize_int4_b256", reordered.nbytes,
+             par(lambda b0, b1: oracle.quantize(reordered[b0 * B:b1 * B], B, 4), reordered.size // B)),
+            ("hop1", g * (Cl // 2 + 4 * Cl // B),
+             par(lambda b0, b1: oracle.dequant_reduce_requant([hc[b0 * B // 2:b1 * B // 2]] * g, [hs[b0:b1]] * g, 4,
+                                                              (b1 - b0) * B, B, 4), Cl // B)),
+            ("hop2", n * (S // 2 + 4 * S // B),
+             par(lambda b0, b1: oracle.dequant_reduce_requant([h2c[b0 * B // 2:b1 * B // 2]] * n, [h2s[b0:b1]] * n,
+                                                              4, (b1 - b0) * B, B, 0), S // B)),
+            ("quantize_int8_b512", 2 * nw,
+             par(lambda b0, b1: oracle.quantize(step.w_np[b0 * 512:b1 * 512], 512, 8), nw // 512)),
+            ("dequantize_int8_b512", nw + 4 * nw // 512,
+             par(lambda b0, b1: oracle.dequantize(w_q[0][b0 * 512:b1 * 512], w_q[1][b0:b1], 8, (b1 - b0) * 512, 512,
+                                                  out="bf16"), nw // 512)),
+            ("quantize_int4_b128", 2 * nw,
+             par(lambda b0, b1: oracle.quantize(step.g_np[b0 * 128:b1 * 128], 128, 4), nw // 128)),
+        ]
+
+    def leg(pool, passes):
+        timings = []
+        for _ in range(passes):
+            for name, nb, fn in work(pool):
+                t = time.perf_counter()
+                fn()
+                timings.append((name, nb, time.perf_counter() - t))
+        total_in = sum(t[1] for t in timings)
+        total_s = sum(t[2] for t in timings)
+        return {"GBps": round(total_in / total_s / 1e9, 4), "seconds": round(total_s, 2),
+                "input_GB": round(total_in / 1e9, 2), "passes": passes,
+                "per_kernel_s": {k: round(sum(t[2] for t in timings if t[0] == k), 3)
+                                 for k in dict.fromkeys(t[0] for t in timings)}}
+
+    one = leg(None, passes_one)
+    with ThreadPoolExecutor(cores) as pool:
+        allc = leg(pool, passes_all)
     return {
-        "value": round(total_in / total_s / 1e9, 4),
+        "value": allc["GBps"],
         "unit": "GB/s",
-        "cores": 1,
+        "cores": cores,
         "kind": "oracle",
-        "sample": (f"{'all' if frac == 1.0 else f'first {frac:g}'} of every kernel's work in one step "
-                   f"({sub_s}-element slices, {hop_n}-element hop-1 chunk, {w_n}/{g_n} GQA elements), "
-                   f"{passes} passes: {total_in / 1e9:.2f} GB of input in {total_s:.1f} s, single-threaded C"),
-        "seconds": round(total_s, 2),
+        "sample": (f"all of every kernel's work in one step ({S}-element slices, {Cl}-element hop-1 chunk, "
+                   f"{nw}-element GQA weight and gradient), {passes_all} passes on {cores} threads over "
+                   f"independent block ranges ({allc['input_GB']} GB of input in {allc['seconds']} s); "
+                   f"one_core: the same work, {passes_one} pass on one thread"),
+        "seconds": allc["seconds"],
         "cpu_model": cpu_model(),
-        "host_cores_available": len(os.sched_getaffinity(0)),
-        "per_kernel_s": {name: round(sum(t[2] for t in timings if t[0] == name), 3)
-                         for name in dict.fromkeys(t[0] for t in timings)},
+        "per_kernel_s": allc["per_kernel_s"],
+        "one_core": {"value": one["GBps"], "unit": "GB/s", "cores": 1, "seconds": one["seconds"],
+                     "per_kernel_s": one["per_kernel_s"]},
     }
+
+
+ROTATE_BYTES = 1 << 30  # input and output copies a smaller-workload row cycles through
 
 
 def configs_bench(torch, z, K: int = 50) -> dict:
     """Kernel times at the three smaller workload shapes (the 500M-element
-    bucket and the GQA layer are the step's rows). Each row is timed with HIP
-    events around K launches (the mean), after one untimed launch."""
+    bucket and the GQA layer are the step's rows). Each row cycles through
+    copies of its inputs and outputs totalling at least 1 GiB, so every launch
+    reads inputs last touched a gigabyte of traffic earlier (out of the
+    256 MB Infinity Cache) and writes outputs that are not resident either;
+    each launch is timed with HIP events (mean, p10, p50, p90 over K
+    launches, after one untimed pass over all copies)."""
+    import math
+
     import numpy as np
 
     import synth
@@ -408,21 +473,33 @@ def configs_bench(torch, z, K: int = 50) -> dict:
         t = torch.from_numpy(np.ascontiguousarray(a))
         return t.view(torch.int16).view(torch.bfloat16).to(dev) if a.dtype == np.uint16 else t.to(dev)
 
+    def nbytes(ts):
+        return sum(t.numel() * t.element_size() for t in ts)
+
     def rows(table):
-        """table: [(name, fn, read bytes, write bytes)] -> {name: timing}"""
+        """table: [(name, buffers, fn(buffers), read bytes, write bytes)] -> {name: timing}"""
         out = {}
-        for name, fn, rb, wb in table:
-            fn()
+        for name, bufs, fn, rb, wb in table:
+            ncopy = max(2, math.ceil(ROTATE_BYTES / nbytes(bufs)))
+            copies = [bufs] + [tuple(t.clone() for t in bufs) for _ in range(ncopy - 1)]
+            for c in copies:
+                fn(c)
             ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-            for a, b in ev:
+            torch.cuda.synchronize()
+            for k, (a, b) in enumerate(ev):
                 a.record(stream)
-                fn()
+                fn(copies[(k + 1) % ncopy])
                 b.record(stream)
             torch.cuda.synchronize()
-            ms = sum(a.elapsed_time(b) for a, b in ev) / K
-            out[name] = {"ms": round(ms, 5), "in_GBps": round(rb / (ms * 1e-3) / 1e9, 1),
-                         "hbm_frac": round((rb + wb) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
-            log(f"{name}: {ms * 1e3:.1f} us, {out[name]['hbm_frac']:.3f} of HBM peak")
+            ts = sorted(a.elapsed_time(b) for a, b in ev)
+            ms = sum(ts) / K
+            out[name] = {"ms": round(ms, 5), "ms_p10": round(ts[int(0.1 * (K - 1))], 5),
+                         "ms_p50": round(ts[(K - 1) // 2], 5), "ms_p90": round(ts[int(0.9 * (K - 1) + 0.5)], 5),
+                         "in_GBps": round(rb / (ms * 1e-3) / 1e9, 1),
+                         "hbm_frac": round((rb + wb) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                         "copies": ncopy, "rotated_bytes": ncopy * nbytes(bufs)}
+            log(f"{name}: {ms * 1e3:.1f} us, {out[name]['hbm_frac']:.3f} of HBM peak ({ncopy} copies)")
+            del copies
         return out
 
     res = {}
@@ -432,12 +509,13 @@ def configs_bench(torch, z, K: int = 50) -> dict:
     x1 = to_dev(c1.weight())
     q1c = torch.empty(n1, dtype=torch.uint8, device=dev)
     q1s = torch.empty(n1 // B1, dtype=torch.float32, device=dev)
+    z.zpp_quantize_blocks(x1, z.ZPP_BF16, n1, B1, 8, q1c, q1s)
     y1 = torch.empty_like(x1)
     res[c1.name] = rows([
-        ("quantize_int8_b256", lambda: z.zpp_quantize_blocks(x1, z.ZPP_BF16, n1, B1, 8, q1c, q1s),
-         2 * n1, n1 + 4 * n1 // B1),
-        ("dequantize_int8_b256_bf16", lambda: z.zpp_dequantize_blocks(q1c, q1s, 8, n1, B1, y1, z.ZPP_BF16),
-         n1 + 4 * n1 // B1, 2 * n1),
+        ("quantize_int8_b256", (x1, q1c, q1s),
+         lambda b: z.zpp_quantize_blocks(b[0], z.ZPP_BF16, n1, B1, 8, b[1], b[2]), 2 * n1, n1 + 4 * n1 // B1),
+        ("dequantize_int8_b256_bf16", (q1c, q1s, y1),
+         lambda b: z.zpp_dequantize_blocks(b[0], b[1], 8, n1, B1, b[2], z.ZPP_BF16), n1 + 4 * n1 // B1, 2 * n1),
     ])
     del x1, q1c, q1s, y1
     # 8 ranks x 16M at 2 x 4, int4 block 128
@@ -450,33 +528,40 @@ def configs_bench(torch, z, K: int = 50) -> dict:
     q2s = torch.empty(N * P // B2, dtype=torch.float32, device=dev)
     h2c = torch.empty(n * P // 2, dtype=torch.uint8, device=dev)
     h2s = torch.empty(n * P // B2, dtype=torch.float32, device=dev)
-
-    def reorder_all():
-        for r in range(N):
-            z.zpp_reorder_slices(grads[r * P:], reord[r * P:], 2 * S, n, g)
-
-    reorder_all()
+    for r in range(N):
+        z.zpp_reorder_slices(grads[r * P:], reord[r * P:], 2 * S, n, g)
     z.zpp_quantize_blocks(reord, z.ZPP_BF16, N * P, B2, 4, q2c, q2s)
     torch.cuda.synchronize()
     a, j = n - 1, g - 1  # rank 7's share: chunk j of node a's local ranks
     one_off = a * g * P + j * C
+    # one GPU's share as it would arrive: its 4 inputs side by side
+    sh_c = q2c.view(N, P // 2)[a * g:(a + 1) * g, j * C // 2:(j + 1) * C // 2].contiguous().view(-1)
+    sh_s = q2s.view(N, P // B2)[a * g:(a + 1) * g, j * C // B2:(j + 1) * C // B2].contiguous().view(-1)
+    o1c = torch.empty(C // 2, dtype=torch.uint8, device=dev)
+    o1s = torch.empty(C // B2, dtype=torch.float32, device=dev)
+    del one_off
 
-    def hop1_all():
+    def reorder_all(b):
+        for r in range(N):
+            z.zpp_reorder_slices(b[0][r * P:], b[1][r * P:], 2 * S, n, g)
+
+    def hop1_all(b):
         for aa in range(n):
-            z.zpp_dequant_reduce_requant(q2c[aa * g * P // 2:], P // 2, q2s[aa * g * P // B2:], P // B2, g, 4, P, B2,
-                                         h2c[aa * P // 2:], h2s[aa * P // B2:], 4, None)
+            z.zpp_dequant_reduce_requant(b[0][aa * g * P // 2:], P // 2, b[1][aa * g * P // B2:], P // B2, g, 4, P,
+                                         B2, b[2][aa * P // 2:], b[3][aa * P // B2:], 4, None)
 
     w1 = g * (C // 2 + 4 * C // B2)
     res[c2.name] = rows([
-        ("reorder_bf16_8_ranks", reorder_all, 2 * N * P, 2 * N * P),
-        ("quantize_int4_b128_8_ranks", lambda: z.zpp_quantize_blocks(reord, z.ZPP_BF16, N * P, B2, 4, q2c, q2s),
+        ("reorder_bf16_8_ranks", (grads, reord), reorder_all, 2 * N * P, 2 * N * P),
+        ("quantize_int4_b128_8_ranks", (reord, q2c, q2s),
+         lambda b: z.zpp_quantize_blocks(b[0], z.ZPP_BF16, N * P, B2, 4, b[1], b[2]),
          2 * N * P, N * P // 2 + 4 * N * P // B2),
-        ("hop1_4way_one_share", lambda: z.zpp_dequant_reduce_requant(
-            q2c[one_off // 2:], P // 2, q2s[one_off // B2:], P // B2, g, 4, C, B2, h2c, h2s, 4, None),
+        ("hop1_4way_one_share", (sh_c, sh_s, o1c, o1s),
+         lambda b: z.zpp_dequant_reduce_requant(b[0], C // 2, b[1], C // B2, g, 4, C, B2, b[2], b[3], 4, None),
          w1, C // 2 + 4 * C // B2),
-        ("hop1_4way_all_8_shares", hop1_all, N * w1, N * (C // 2 + 4 * C // B2)),
+        ("hop1_4way_all_8_shares", (q2c, q2s, h2c, h2s), hop1_all, N * w1, N * (C // 2 + 4 * C // B2)),
     ])
-    del grads, reord, q2c, q2s, h2c, h2s
+    del grads, reord, q2c, q2s, h2c, h2s, sh_c, sh_s, o1c, o1s
     # 64 int8 shards (block 2048) of a Llama-style layer, dequantized in one launch
     c3 = synth.QWZ_DEQUANT_64
     n3, B3 = c3.numel, c3.block
@@ -484,10 +569,11 @@ def configs_bench(torch, z, K: int = 50) -> dict:
     q3c = torch.empty(n3, dtype=torch.uint8, device=dev)
     q3s = torch.empty(n3 // B3, dtype=torch.float32, device=dev)
     z.zpp_quantize_blocks(x3, z.ZPP_BF16, n3, B3, 8, q3c, q3s)
-    y3 = torch.empty_like(x3)
+    del x3
+    y3 = torch.empty(n3, dtype=torch.bfloat16, device=dev)
     res[c3.name] = rows([
-        ("dequantize_int8_b2048_64_shards", lambda: z.zpp_dequantize_blocks(q3c, q3s, 8, n3, B3, y3, z.ZPP_BF16),
-         n3 + 4 * n3 // B3, 2 * n3),
+        ("dequantize_int8_b2048_64_shards", (q3c, q3s, y3),
+         lambda b: z.zpp_dequantize_blocks(b[0], b[1], 8, n3, B3, b[2], z.ZPP_BF16), n3 + 4 * n3 // B3, 2 * n3),
     ])
     return res
 

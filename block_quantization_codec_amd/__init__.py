@@ -44,7 +44,8 @@ ZPP_MAX_DIVISOR = 1 << 24
 ZPP_MAX_NUMEL = 1 << 40
 
 EXPORTED = ("zpp_quantize_blocks", "zpp_quantize_reordered", "zpp_dequantize_blocks", "zpp_reorder_slices",
-            "zpp_dequant_reduce_requant", "zpp_dequant_reduce_average", "zpp_status_string", "zpp_abi_version")
+            "zpp_dequant_reduce_requant", "zpp_dequant_reduce_requant_split", "zpp_dequant_reduce_average",
+            "zpp_status_string", "zpp_abi_version")
 
 
 class ZppError(RuntimeError):
@@ -66,6 +67,7 @@ def _load() -> ctypes.CDLL:
         "zpp_dequantize_blocks": [P, P, I32, I64, I32, P, I32, P],
         "zpp_reorder_slices": [P, P, I64, I32, I32, P],
         "zpp_dequant_reduce_requant": [P, I64, P, I64, I32, I32, I64, I32, P, P, I32, P, P],
+        "zpp_dequant_reduce_requant_split": [P, I64, P, I64, I32, I32, I64, I32, I64, I64, P, P, P, P, I32, P],
         "zpp_dequant_reduce_average": [P, I64, P, I64, I32, I32, I64, I32, I32, P, P],
     }
     for name, args in sig.items():
@@ -138,6 +140,14 @@ def zpp_dequant_reduce_requant(codes_in, codes_stride_bytes, scales_in, scales_s
     _call("zpp_dequant_reduce_requant", _ptr(codes_in), codes_stride_bytes, _ptr(scales_in), scales_stride,
           n_inputs, bits_in, numel, block, _ptr(codes_out), _ptr(scales_out), bits_out, _ptr(sum_out),
           _stream(stream))
+
+
+def zpp_dequant_reduce_requant_split(codes_in, codes_stride_bytes, scales_in, scales_stride, n_inputs, bits_in,
+                                     numel, block, keep_begin, keep_elems, codes_send, scales_send, codes_keep,
+                                     scales_keep, bits_out, stream=None) -> None:
+    _call("zpp_dequant_reduce_requant_split", _ptr(codes_in), codes_stride_bytes, _ptr(scales_in), scales_stride,
+          n_inputs, bits_in, numel, block, keep_begin, keep_elems, _ptr(codes_send), _ptr(scales_send),
+          _ptr(codes_keep), _ptr(scales_keep), bits_out, _stream(stream))
 
 
 def zpp_dequant_reduce_average(codes_in, codes_stride_bytes, scales_in, scales_stride, n_inputs, bits_in, numel,

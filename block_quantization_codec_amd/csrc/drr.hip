@@ -37,6 +37,19 @@ hipError_t launch_drr(const void *codes_in, int64_t codes_stride, const float *s
                             sum_out, 0.0f, stream});
 }
 
+hipError_t launch_drr_split(const void *codes_in, int64_t codes_stride, const float *scales_in,
+                            int64_t scales_stride, int n_inputs, int bits_in, int64_t numel, int log2b,
+                            int64_t keep_begin, int64_t keep_len, void *codes_send, float *scales_send,
+                            void *codes_keep, float *scales_keep, int bits_out, hipStream_t stream) {
+    DrrArgs a{codes_in, codes_stride, scales_in, scales_stride, n_inputs, numel, codes_send, scales_send,
+              nullptr, 0.0f, stream};
+    a.keep_begin = keep_begin;
+    a.keep_len = keep_len;
+    a.codes_keep = codes_keep;
+    a.scales_keep = scales_keep;
+    return dispatch(bits_in, bits_out, log2b, a);
+}
+
 hipError_t launch_drr_average(const void *codes_in, int64_t codes_stride, const float *scales_in,
                               int64_t scales_stride, int n_inputs, int bits_in, int64_t numel, int log2b,
                               int divisor, float *avg_out, hipStream_t stream) {

@@ -50,6 +50,14 @@ struct DrrArgs {
     float *sum_out;
     float divisor;
     hipStream_t stream;
+    // Keep window: requantized codes and scales of elements [keep_begin,
+    // keep_begin + keep_len) go to codes_keep / scales_keep, all others to
+    // codes_out / scales_out in order with the window left out (keep_len 0:
+    // no window).
+    int64_t keep_begin = 0;
+    int64_t keep_len = 0;
+    void *codes_keep = nullptr;
+    float *scales_keep = nullptr;
 };
 
 // One launcher per pair of code widths, each in a translation unit of its own
@@ -276,6 +284,27 @@ __device__ __forceinline__ void load_batch(const uint8_t *__restrict__ codes_in,
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// The largest |s| of a batch of scales: float maxima with absolute-value
+// operand modifiers, three values per instruction. An infinite scale makes it
+// infinite; a NaN scale may be dropped, which is harmless: every product with
+// it is NaN under either formula.
+template <typename G, int NB>
+__device__ __forceinline__ float batch_abs_max(const float (&s)[NB][G::U]) {
+    float m = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NB; ++k)
+#pragma unroll
+        for (int u = 0; u < G::U; ++u) m = __builtin_fmaxf(m, __builtin_fabsf(s[k][u]));
+    return m;
+}
+
+// Whether the fused product shortcut of dequant_dword is exact for every
+// scale of magnitude at most m (a NaN m takes the plain product).
+template <int BITS_IN>
+__device__ __forceinline__ bool shortcut_exact(float m) {
+    return m <= (BITS_IN == 8 ? 0x1p120f : 0x1p103f);
+}
+
 // Add a loaded batch into acc, in input order. FIRST: the batch's first input
 // starts the sums, written acc = p instead of acc = +0 + p. The two differ
 // only when p is -0 (a negative code times a zero scale, or a zero code times
@@ -285,15 +314,7 @@ __device__ __forceinline__ void load_batch(const uint8_t *__restrict__ codes_in,
 // requantized sum gets the same codes and scale either way.
 template <typename G, int NB, bool FIRST>
 __device__ __forceinline__ void add_batch(const Batch<G, NB> &b, float (&acc)[G::U][G::E], int valid = NB) {
-    // The largest |s| of the batch, as its bit pattern without the sign
-    // shifted left by one: that orders like |s|, with infinities and NaNs
-    // above every finite value.
-    uint32_t hi = 0u;
-#pragma unroll
-    for (int k = 0; k < NB; ++k)
-#pragma unroll
-        for (int u = 0; u < G::U; ++u) hi = max(hi, as_u(b.s[k][u]) << 1);
-    const bool fast = hi <= (as_u(G::BITS_IN == 8 ? 0x1p120f : 0x1p103f) << 1);  // the shortcut is exact
+    const bool fast = shortcut_exact<G::BITS_IN>(batch_abs_max<G, NB>(b.s));
     if (fast)
         accumulate<G, NB, FIRST, true>(b.w, b.s, acc, valid);
     else
@@ -445,12 +466,7 @@ __device__ __forceinline__ void consume_lds(const uint8_t *__restrict__ codes_in
         // The batch's choice of product formula (see add_batch). Taking it
         // here makes the compiler wait for the scales before the loads into
         // LDS are issued, so that only those are outstanding below.
-        uint32_t hi = 0u;
-#pragma unroll
-        for (int k = 0; k < NB; ++k)
-#pragma unroll
-            for (int u = 0; u < G::U; ++u) hi = max(hi, as_u(s[k][u]) << 1);
-        const bool fast = hi <= (as_u(0x1p103f) << 1);
+        const bool fast = shortcut_exact<4>(batch_abs_max<G, NB>(s));
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int k = 0; k < NB; ++k) {
@@ -483,16 +499,87 @@ constexpr int drr_min_waves() {
                : 1;
 }
 
+// Where one launch writes. Sums (or averages) go to sum_out. Requantized
+// codes and scales of the elements in the keep window [kb, kb + klen) go to
+// codes_keep / scales_keep (element kb first); all others go to codes_out /
+// scales_out in element order with the window left out. klen == 0: no
+// window. kb and klen are whole blocks.
+struct DrrOut {
+    uint8_t *codes_out;
+    float *scales_out;
+    float *sum_out;
+    float divisor;
+    uint32_t kb, klen;
+    uint8_t *codes_keep;
+    float *scales_keep;
+};
+
+// The end of a tile: the sums (plus +0, see add_batch), or their averages,
+// stored; then the sums requantized per block and stored.
+template <typename G, int BITS_OUT, bool AVG>
+__device__ __forceinline__ void finish_tile(float (&acc)[G::U][G::E], const bool (&ok)[G::U],
+                                            const uint32_t (&e)[G::U], int lane, const DrrOut &out) {
+    static_assert(!AVG || BITS_OUT == 0, "the average is a final binary32 output");
+    constexpr int U = G::U, E = G::E;
+    if (AVG || out.sum_out != nullptr) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int i = 0; i < E; ++i) {
+                float v = acc[u][i] + 0.0f;          // -0 -> +0 (see add_batch), any other value unchanged
+                if constexpr (AVG) v = v / out.divisor;  // IEEE division
+                acc[u][i] = v;
+            }
+    }
+    if (out.sum_out != nullptr) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (!ok[u]) continue;
+            float *dst = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(out.sum_out) + e[u] * 4u);
+#pragma unroll
+            for (int v = 0; v < E / 4; ++v)
+                st_out<u32x4>(dst + 4 * v, u32x4{as_u(acc[u][4 * v]), as_u(acc[u][4 * v + 1]),
+                                             as_u(acc[u][4 * v + 2]), as_u(acc[u][4 * v + 3])});
+        }
+    }
+    if constexpr (BITS_OUT != 0) {
+        // |acc| maximum as a float maximum with abs operand modifiers (three
+        // values per instruction); for non-negative finite values it
+        // equals the integer maximum of the bit patterns.
+        float fm = 0.0f;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int i = 0; i < E; ++i) fm = __builtin_fmaxf(fm, __builtin_fabsf(acc[u][i]));
+        uint32_t mx = ok[0] ? as_u(fm) : 0u;
+        mx = group_max_u32<G::L>(mx);
+        const float sc = block_scale<G::QMAX>(as_f(mx));
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float mg[E];
+            round_codes<E, BITS_OUT>(acc[u], sc, mg);
+            uint32_t cw[E * BITS_OUT / 32];
+            pack_codes<E, BITS_OUT>(mg, cw);
+            if (!ok[u]) continue;
+            // output position: inside the keep window, or in the rest with the window left out
+            const uint32_t rel = e[u] - out.kb;
+            const bool keep = rel < out.klen;
+            const uint32_t idx = keep ? rel : (e[u] < out.kb ? e[u] : e[u] - out.klen);
+            uint8_t *cdst = keep ? out.codes_keep : out.codes_out;
+            float *sdst = keep ? out.scales_keep : out.scales_out;
+            store_dwords<E * BITS_OUT / 32>(cdst + idx * BITS_OUT / 8, cw);
+            if (u == 0 && (lane & (G::L - 1)) == 0) sdst[idx >> G::LOG2B] = sc;
+        }
+    }
+}
+
 template <int BITS_IN, int BITS_OUT, int LOG2B, int E, bool AVG>
 __global__ __launch_bounds__(kBlockThreads)
 __attribute__((amdgpu_waves_per_eu(drr_min_waves<BITS_IN, LOG2B, E>(), 8))) void drr_kernel(const uint8_t *__restrict__ codes_in,
                                                             int64_t codes_stride,
                                                             const float *__restrict__ scales_in,
                                                             int64_t scales_stride, int n_inputs, int numel,
-                                                            uint8_t *__restrict__ codes_out,
-                                                            float *__restrict__ scales_out,
-                                                            float *__restrict__ sum_out, float divisor) {
-    static_assert(!AVG || BITS_OUT == 0, "the average is a final binary32 output");
+                                                            DrrOut out) {
     using G = DrrGeom<BITS_IN, BITS_OUT, LOG2B, E>;
     constexpr int U = G::U;
 
@@ -539,54 +626,32 @@ __attribute__((amdgpu_waves_per_eu(drr_min_waves<BITS_IN, LOG2B, E>(), 8))) void
         } else {
             consume_padded<G, G::RB>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, o, acc);
         }
-
-        if (AVG || sum_out != nullptr) {
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-#pragma unroll
-                for (int i = 0; i < E; ++i) {
-                    float v = acc[u][i] + 0.0f;      // -0 -> +0 (see add_batch), any other value unchanged
-                    if constexpr (AVG) v = v / divisor;  // IEEE division
-                    acc[u][i] = v;
-                }
-        }
-        if (sum_out != nullptr) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                if (!ok[u]) continue;
-                float *dst = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(sum_out) + e[u] * 4u);
-#pragma unroll
-                for (int v = 0; v < E / 4; ++v)
-                    st_out<u32x4>(dst + 4 * v, u32x4{as_u(acc[u][4 * v]), as_u(acc[u][4 * v + 1]),
-                                                 as_u(acc[u][4 * v + 2]), as_u(acc[u][4 * v + 3])});
-            }
-        }
-
-        if constexpr (BITS_OUT != 0) {
-            // |acc| maximum as a float maximum with abs operand modifiers (three
-            // values per instruction); for non-negative finite values it
-            // equals the integer maximum of the bit patterns.
-            float fm = 0.0f;
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-#pragma unroll
-                for (int i = 0; i < E; ++i) fm = __builtin_fmaxf(fm, __builtin_fabsf(acc[u][i]));
-            uint32_t mx = ok[0] ? as_u(fm) : 0u;
-            mx = group_max_u32<G::L>(mx);
-            const float sc = block_scale<G::QMAX>(as_f(mx));
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float mg[E];
-                round_codes<E, BITS_OUT>(acc[u], sc, mg);
-                uint32_t cw[E * BITS_OUT / 32];
-                pack_codes<E, BITS_OUT>(mg, cw);
-                if (!ok[u]) continue;
-                store_dwords<E * BITS_OUT / 32>(codes_out + e[u] * BITS_OUT / 8, cw);
-                if (u == 0 && (lane & (G::L - 1)) == 0)
-                    *reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(scales_out) + o.scale[0]) = sc;
-            }
-        }
+        finish_tile<G, BITS_OUT, AVG>(acc, ok, e, lane, out);
     }
+}
+
+// The outputs of the launch covering elements [done, done + n): the keep
+// window clipped to it, and each output's base for its first element.
+template <int BITS_OUT, int LOG2B>
+DrrOut chunk_out(const DrrArgs &a, int64_t done, int64_t n) {
+    const int64_t k0 = a.keep_begin, k1 = a.keep_begin + a.keep_len;
+    const int64_t kb = k0 - done < 0 ? 0 : (k0 - done > n ? n : k0 - done);
+    const int64_t ke = k1 - done < 0 ? 0 : (k1 - done > n ? n : k1 - done);
+    // elements before `done` that sit in the window
+    const int64_t skipped = done - k0 < 0 ? 0 : (done - k0 > a.keep_len ? a.keep_len : done - k0);
+    const int64_t send0 = done - skipped;   // output position of the chunk's first element outside the window
+    const int64_t keep0 = done + kb - k0;   // keep position of the chunk's first element inside it
+    DrrOut o;
+    o.codes_out = a.codes_out ? static_cast<uint8_t *>(a.codes_out) + send0 * BITS_OUT / 8 : nullptr;
+    o.scales_out = a.scales_out ? a.scales_out + (send0 >> LOG2B) : nullptr;
+    o.sum_out = a.sum_out ? a.sum_out + done : nullptr;
+    o.divisor = a.divisor;
+    o.kb = static_cast<uint32_t>(kb);
+    o.klen = static_cast<uint32_t>(ke - kb);
+    const bool win = a.keep_len > 0 && ke > kb;
+    o.codes_keep = win ? static_cast<uint8_t *>(a.codes_keep) + keep0 * BITS_OUT / 8 : nullptr;
+    o.scales_keep = win ? a.scales_keep + (keep0 >> LOG2B) : nullptr;
+    return o;
 }
 
 // One launch per chunk of at most kDrrChunk elements (blocks are independent).
@@ -596,12 +661,11 @@ hipError_t launch_e(const DrrArgs &a) {
     for (int64_t done = 0; done < a.numel; done += kDrrChunk) {
         const int64_t n = a.numel - done < kDrrChunk ? a.numel - done : kDrrChunk;
         const int64_t tiles = (n + G::TILE - 1) / G::TILE;
+        const uint8_t *ci = static_cast<const uint8_t *>(a.codes_in) + done * BITS_IN / 8;
+        const float *si = a.scales_in + (done >> LOG2B);
+        const DrrOut o = chunk_out<BITS_OUT, LOG2B>(a, done, n);
         drr_kernel<BITS_IN, BITS_OUT, LOG2B, E, AVG><<<stream_grid(tiles), kBlockThreads, 0, a.stream>>>(
-            static_cast<const uint8_t *>(a.codes_in) + done * BITS_IN / 8, a.cstride, a.scales_in + (done >> LOG2B),
-            a.sstride, a.n_inputs, static_cast<int>(n),
-            a.codes_out ? static_cast<uint8_t *>(a.codes_out) + done * BITS_OUT / 8 : nullptr,
-            a.scales_out ? a.scales_out + (done >> LOG2B) : nullptr, a.sum_out ? a.sum_out + done : nullptr,
-            a.divisor);
+            ci, a.cstride, si, a.sstride, a.n_inputs, static_cast<int>(n), o);
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }

@@ -272,6 +272,49 @@ zpp_status zpp_dequant_reduce_requant(const void *codes_in, int64_t codes_stride
     });
 }
 
+zpp_status zpp_dequant_reduce_requant_split(const void *codes_in, int64_t codes_stride_bytes, const float *scales_in,
+                                            int64_t scales_stride, int32_t n_inputs, int32_t bits_in, int64_t numel,
+                                            int32_t block, int64_t keep_begin, int64_t keep_elems, void *codes_send,
+                                            float *scales_send, void *codes_keep, float *scales_keep,
+                                            int32_t bits_out, void *stream) {
+    if (bits_in != 8 && bits_in != 4) return ZPP_ERR_ARG;
+    if (bits_out != 8 && bits_out != 4) return ZPP_ERR_ARG;
+    if (!is_pow2_block(block) || numel < 0 || numel > ZPP_MAX_NUMEL || numel % block != 0) return ZPP_ERR_ARG;
+    if (n_inputs < 1 || n_inputs > ZPP_MAX_INPUTS) return ZPP_ERR_ARG;
+    if (codes_stride_bytes < 0 || codes_stride_bytes > ZPP_MAX_NUMEL) return ZPP_ERR_ARG;
+    if (scales_stride < 0 || scales_stride > ZPP_MAX_NUMEL) return ZPP_ERR_ARG;
+    if (keep_begin < 0 || keep_elems < 0 || keep_begin > numel || keep_elems > numel - keep_begin) return ZPP_ERR_ARG;
+    if (keep_begin % block != 0 || keep_elems % block != 0) return ZPP_ERR_ARG;
+    if (numel == 0) return ZPP_OK;
+    const int64_t send_elems = numel - keep_elems;
+    if (!codes_in || !scales_in) return ZPP_ERR_NULL;
+    if (send_elems > 0 && (!codes_send || !scales_send)) return ZPP_ERR_NULL;
+    if (keep_elems > 0 && (!codes_keep || !scales_keep)) return ZPP_ERR_NULL;
+    if (!aligned(codes_in, 16) || (codes_stride_bytes & 15) != 0 || !aligned(scales_in, 4)) return ZPP_ERR_ALIGN;
+    if (send_elems > 0 && (!aligned(codes_send, 16) || !aligned(scales_send, 4))) return ZPP_ERR_ALIGN;
+    if (keep_elems > 0 && (!aligned(codes_keep, 16) || !aligned(scales_keep, 4))) return ZPP_ERR_ALIGN;
+    const int64_t nblk = numel / block;
+    const Range ic{codes_in, (n_inputs - 1) * codes_stride_bytes + code_bytes(numel, bits_in)},
+        is{scales_in, 4 * ((n_inputs - 1) * scales_stride + nblk)},
+        oc{codes_send, code_bytes(send_elems, bits_out)}, os{scales_send, 4 * (send_elems / block)},
+        kc{codes_keep, code_bytes(keep_elems, bits_out)}, ks{scales_keep, 4 * (keep_elems / block)};
+    const Range outs[] = {oc, os, kc, ks};
+    for (const Range &o : outs) {
+        if (overlap(o, ic) || overlap(o, is)) return ZPP_ERR_OVERLAP;
+    }
+    for (int i = 0; i < 4; ++i)
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], outs[j])) return ZPP_ERR_OVERLAP;
+    const Range all[] = {ic, is, oc, os, kc, ks};
+    if (zpp_status s = check_all(all); s != ZPP_OK) return s;
+    return launch_checked([&] {
+        return zpp::launch_drr_split(codes_in, codes_stride_bytes, scales_in, scales_stride, n_inputs, bits_in, numel,
+                   log2_of(block), keep_begin, keep_elems, send_elems > 0 ? codes_send : nullptr,
+                   send_elems > 0 ? scales_send : nullptr, keep_elems > 0 ? codes_keep : nullptr,
+                   keep_elems > 0 ? scales_keep : nullptr, bits_out, static_cast<hipStream_t>(stream));
+    });
+}
+
 zpp_status zpp_dequant_reduce_average(const void *codes_in, int64_t codes_stride_bytes, const float *scales_in,
                                       int64_t scales_stride, int32_t n_inputs, int32_t bits_in, int64_t numel,
                                       int32_t block, int32_t divisor, float *avg_out, void *stream) {

@@ -24,6 +24,11 @@ hipError_t launch_drr(const void *codes_in, int64_t codes_stride, const float *s
                       int n_inputs, int bits_in, int64_t numel, int log2b, void *codes_out, float *scales_out,
                       int bits_out, float *sum_out, hipStream_t stream);
 
+hipError_t launch_drr_split(const void *codes_in, int64_t codes_stride, const float *scales_in,
+                            int64_t scales_stride, int n_inputs, int bits_in, int64_t numel, int log2b,
+                            int64_t keep_begin, int64_t keep_len, void *codes_send, float *scales_send,
+                            void *codes_keep, float *scales_keep, int bits_out, hipStream_t stream);
+
 hipError_t launch_drr_average(const void *codes_in, int64_t codes_stride, const float *scales_in,
                               int64_t scales_stride, int n_inputs, int bits_in, int64_t numel, int log2b,
                               int divisor, float *avg_out, hipStream_t stream);

@@ -221,6 +221,38 @@ zpp_status zpp_dequant_reduce_requant(const void *codes_in, int64_t codes_stride
                                       int32_t bits_out, float *sum_out, void *stream);
 
 /*
+ * The hop-1 step of qgZ [QGZ] with its output split the way the next hop
+ * needs it: the same binary32 input-order sum as zpp_dequant_reduce_requant,
+ * requantized, with the requantized codes and scales of the elements in
+ * [keep_begin, keep_begin + keep_elems) written to codes_keep / scales_keep
+ * (the piece this GPU keeps for itself in hop 2: its own sub-chunk, which
+ * goes straight into its slot of the hop-2 receive buffer), and those of
+ * all other elements written to codes_send / scales_send, in element order
+ * with the kept window left out (what the inter-node all-to-all sends). One
+ * pass over the inputs; both outputs are exactly the corresponding parts of
+ * zpp_dequant_reduce_requant's output.
+ *
+ *   codes_in, codes_stride_bytes, scales_in, scales_stride, n_inputs,
+ *   bits_in, numel, block   in   as zpp_dequant_reduce_requant
+ *   keep_begin, keep_elems  in   the kept window, whole blocks:
+ *                                0 <= keep_begin <= keep_begin + keep_elems <= numel
+ *   codes_send   out  (numel - keep_elems) * bits_out / 8 bytes, 16-B aligned
+ *   scales_send  out  (numel - keep_elems) / block floats, 4-B aligned
+ *                     (both may be NULL when keep_elems == numel)
+ *   codes_keep   out  keep_elems * bits_out / 8 bytes, 16-B aligned
+ *   scales_keep  out  keep_elems / block floats, 4-B aligned
+ *                     (both may be NULL when keep_elems == 0)
+ *   bits_out     in   8 or 4
+ *   stream       in   hipStream_t
+ */
+zpp_status zpp_dequant_reduce_requant_split(const void *codes_in, int64_t codes_stride_bytes,
+                                            const float *scales_in, int64_t scales_stride,
+                                            int32_t n_inputs, int32_t bits_in, int64_t numel,
+                                            int32_t block, int64_t keep_begin, int64_t keep_elems,
+                                            void *codes_send, float *scales_send, void *codes_keep,
+                                            float *scales_keep, int32_t bits_out, void *stream);
+
+/*
  * The final hop of qgZ writing the optimizer-ready shard [QGZ][AVG]: the same
  * input-order binary32 sum as zpp_dequant_reduce_requant, then divided by
  * `divisor`, the number of GPUs whose gradients the sum holds (for the

@@ -10,7 +10,10 @@
  *   <dir>/x.bin       n bf16 values (uint16), n = 8 slices of S elements
  *   <dir>/params.txt  "n S block"
  * writes <dir>/codes8.bin scales8.bin y.bin reordered.bin codes4.bin
- *        scales4.bin sum.bin hop_codes.bin hop_scales.bin avg.bin status.txt
+ *        scales4.bin fused_codes.bin fused_scales.bin sum.bin hop_codes.bin
+ *        hop_scales.bin send_codes.bin send_scales.bin keep_codes.bin
+ *        keep_scales.bin avg.bin status.txt
+ * The split hop keeps blocks [10, 17) of the S-element output.
  */
 #include <stdint.h>
 #include <stdio.h>
@@ -62,8 +65,10 @@ int main(int argc, char **argv) {
 
     hipStream_t st;
     HIP_OK(hipStreamCreate(&st));
-    void *x, *codes8, *y, *reord, *codes4, *hop_codes;
-    float *scales8, *scales4, *sum, *hop_scales, *avg;
+    void *x, *codes8, *y, *reord, *codes4, *hop_codes, *fused_codes, *send_codes, *keep_codes;
+    float *scales8, *scales4, *sum, *hop_scales, *avg, *fused_scales, *send_scales, *keep_scales;
+    const long long K0 = 10 * B, KL = 7 * B; /* kept window of the split hop */
+    if (S < K0 + KL) return fail("params", 0);
     HIP_OK(hipMalloc(&x, (size_t)n * 2));
     HIP_OK(hipMalloc(&codes8, (size_t)n));
     HIP_OK(hipMalloc((void **)&scales8, (size_t)(n / B) * 4));
@@ -75,6 +80,12 @@ int main(int argc, char **argv) {
     HIP_OK(hipMalloc(&hop_codes, (size_t)S / 2));
     HIP_OK(hipMalloc((void **)&hop_scales, (size_t)(S / B) * 4));
     HIP_OK(hipMalloc((void **)&avg, (size_t)S * 4));
+    HIP_OK(hipMalloc(&fused_codes, (size_t)n / 2));
+    HIP_OK(hipMalloc((void **)&fused_scales, (size_t)(n / B) * 4));
+    HIP_OK(hipMalloc(&send_codes, (size_t)(S - KL) / 2));
+    HIP_OK(hipMalloc((void **)&send_scales, (size_t)((S - KL) / B) * 4));
+    HIP_OK(hipMalloc(&keep_codes, (size_t)KL / 2));
+    HIP_OK(hipMalloc((void **)&keep_scales, (size_t)(KL / B) * 4));
     HIP_OK(hipMemcpy(x, xh, (size_t)n * 2, hipMemcpyHostToDevice));
 
     /* qwZ: 8-bit quantize and dequantize back to bf16 */
@@ -83,9 +94,13 @@ int main(int argc, char **argv) {
     /* qgZ on a 2-node x 4-GPU grid: reorder, 4-bit quantize of the reordered buffer */
     ZPP_OK_(zpp_reorder_slices(x, reord, S * 2, 2, 4, st));
     ZPP_OK_(zpp_quantize_blocks(reord, ZPP_BF16, n, (int32_t)B, 4, codes4, scales4, st));
+    /* the same, with the reorder fused into the quantize */
+    ZPP_OK_(zpp_quantize_reordered(x, ZPP_BF16, S, 2, 4, 0, 8, (int32_t)B, 4, fused_codes, fused_scales, st));
     /* reduce the 8 quantized slices as 8 inputs: sum, requantized sum, average */
     ZPP_OK_(zpp_dequant_reduce_requant(codes4, S / 2, scales4, S / B, 8, 4, S, (int32_t)B, hop_codes, hop_scales, 4,
                                        sum, st));
+    ZPP_OK_(zpp_dequant_reduce_requant_split(codes4, S / 2, scales4, S / B, 8, 4, S, (int32_t)B, K0, KL, send_codes,
+                                             send_scales, keep_codes, keep_scales, 4, st));
     ZPP_OK_(zpp_dequant_reduce_average(codes4, S / 2, scales4, S / B, 8, 4, S, (int32_t)B, 8, avg, st));
     HIP_OK(hipStreamSynchronize(st));
 
@@ -103,6 +118,12 @@ int main(int argc, char **argv) {
     rc |= save(dir, "hop_codes.bin", hop_codes, (size_t)S / 2);
     rc |= save(dir, "hop_scales.bin", hop_scales, (size_t)(S / B) * 4);
     rc |= save(dir, "avg.bin", avg, (size_t)S * 4);
+    rc |= save(dir, "fused_codes.bin", fused_codes, (size_t)n / 2);
+    rc |= save(dir, "fused_scales.bin", fused_scales, (size_t)(n / B) * 4);
+    rc |= save(dir, "send_codes.bin", send_codes, (size_t)(S - KL) / 2);
+    rc |= save(dir, "send_scales.bin", send_scales, (size_t)((S - KL) / B) * 4);
+    rc |= save(dir, "keep_codes.bin", keep_codes, (size_t)KL / 2);
+    rc |= save(dir, "keep_scales.bin", keep_scales, (size_t)(KL / B) * 4);
     snprintf(path, sizeof path, "%s/status.txt", dir);
     FILE *sf = fopen(path, "w");
     if (!sf) return fail("status.txt", 0);
@@ -111,6 +132,8 @@ int main(int argc, char **argv) {
 
     hipFree(x); hipFree(codes8); hipFree(scales8); hipFree(y); hipFree(reord); hipFree(codes4);
     hipFree(scales4); hipFree(sum); hipFree(hop_codes); hipFree(hop_scales); hipFree(avg);
+    hipFree(fused_codes); hipFree(fused_scales); hipFree(send_codes); hipFree(send_scales);
+    hipFree(keep_codes); hipFree(keep_scales);
     hipStreamDestroy(st);
     free(xh);
     return rc;

@@ -189,6 +189,44 @@ def test_drr_argument_errors(z):
     assert call(n=0) == z.ZPP_OK
 
 
+def test_drr_split_argument_errors(z):
+    f = z.library().zpp_dequant_reduce_requant_split
+    C, S, O, OS, K, KS = A, A + (1 << 24), A + (1 << 25), A + (1 << 26), A + (1 << 27), A + (1 << 28)
+    ok = dict(ci=C, cs=1 << 16, si=S, ss=1 << 10, R=8, bi=4, n=1 << 12, B=256, kb=1024, kl=512, co=O, so=OS,
+              kc=K, ks=KS, bo=4)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["ci"], a["cs"], a["si"], a["ss"], a["R"], a["bi"], a["n"], a["B"], a["kb"], a["kl"], a["co"],
+                 a["so"], a["kc"], a["ks"], a["bo"], None)
+
+    assert call(bi=2) == z.ZPP_ERR_ARG
+    assert call(bo=0) == z.ZPP_ERR_ARG                       # the split step always requantizes
+    assert call(bo=16) == z.ZPP_ERR_ARG
+    assert call(R=0) == z.ZPP_ERR_ARG
+    assert call(n=300) == z.ZPP_ERR_ARG
+    assert call(B=48) == z.ZPP_ERR_ARG
+    assert call(kb=-256) == z.ZPP_ERR_ARG
+    assert call(kl=-256) == z.ZPP_ERR_ARG
+    assert call(kb=128) == z.ZPP_ERR_ARG                     # window not whole blocks
+    assert call(kl=100) == z.ZPP_ERR_ARG
+    assert call(kb=4096, kl=256) == z.ZPP_ERR_ARG            # window past the end
+    assert call(kb=1 << 62, kl=1 << 62) == z.ZPP_ERR_ARG     # no wrap-around in the end check
+    assert call(kb=0, kl=(1 << 12) + 256) == z.ZPP_ERR_ARG
+    assert call(ci=None) == z.ZPP_ERR_NULL
+    assert call(co=None) == z.ZPP_ERR_NULL                   # elements left to send
+    assert call(ks=None) == z.ZPP_ERR_NULL                   # a window to keep
+    assert call(cs=8) == z.ZPP_ERR_ALIGN
+    assert call(kc=K + 4) == z.ZPP_ERR_ALIGN
+    assert call(so=OS + 2) == z.ZPP_ERR_ALIGN
+    assert call(kc=C + 64) == z.ZPP_ERR_OVERLAP              # output inside an input
+    assert call(ks=O + 16) == z.ZPP_ERR_OVERLAP              # outputs overlap each other
+    assert call(kc=OS) == z.ZPP_ERR_OVERLAP
+    assert call(n=0) == z.ZPP_ERR_ARG                        # the window no longer fits
+    assert call(n=0, kb=0, kl=0) == z.ZPP_OK
+    assert call(n=0, kb=0, kl=0, ci=None, co=None, kc=None) == z.ZPP_OK
+
+
 def test_drr_average_argument_errors(z):
     f = z.library().zpp_dequant_reduce_average
     C, S, U = A, A + (1 << 24), A + (1 << 27)

@@ -1,7 +1,8 @@
 """The codec used from plain C: tests/c_client/zpp_client.c.
 
 The client (built by ``__graft_entry__.build()``) allocates with hipMalloc,
-calls every entry point through ``include/zpp.h`` on a stream of its own and
+calls every entry point through ``include/zpp.h`` (the fused reorder +
+quantize and the split hop step included) on a stream of its own and
 writes the results to files; this test feeds it a seeded input, runs it as a
 child process and compares everything with the oracle bit for bit. It also
 checks the client saw ordinary host memory refused with ZPP_ERR_POINTER.
@@ -57,6 +58,15 @@ def test_c_client_matches_oracle(tmp_path):
     assert_bits_equal(read("hop_codes.bin", np.uint8), co, "hop codes")
     assert_bits_equal(read("hop_scales.bin", np.float32), so, "hop scales")
     assert_bits_equal(read("avg.bin", np.float32), oracle.dequant_average(cl, sl, 4, S, B, 8), "average")
+    assert_bits_equal(read("fused_codes.bin", np.uint8), c4, "fused reorder+quantize codes")
+    assert_bits_equal(read("fused_scales.bin", np.float32), s4, "fused reorder+quantize scales")
+    k0, k1 = 10 * B, 17 * B  # the split hop's kept window
+    assert_bits_equal(read("keep_codes.bin", np.uint8), co[k0 // 2:k1 // 2], "split hop kept codes")
+    assert_bits_equal(read("keep_scales.bin", np.float32), so[k0 // B:k1 // B], "split hop kept scales")
+    assert_bits_equal(read("send_codes.bin", np.uint8), np.concatenate([co[:k0 // 2], co[k1 // 2:]]),
+                      "split hop sent codes")
+    assert_bits_equal(read("send_scales.bin", np.float32), np.concatenate([so[:k0 // B], so[k1 // B:]]),
+                      "split hop sent scales")
     status = dict(line.split() for line in (tmp_path / "status.txt").read_text().splitlines())
     assert int(status["host_pointer"]) == z.ZPP_ERR_POINTER
     assert int(status["abi"]) == z.zpp_abi_version()
