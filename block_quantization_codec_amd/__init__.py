@@ -45,7 +45,7 @@ ZPP_MAX_NUMEL = 1 << 40
 
 EXPORTED = ("zpp_quantize_blocks", "zpp_quantize_reordered", "zpp_dequantize_blocks", "zpp_reorder_slices",
             "zpp_dequant_reduce_requant", "zpp_dequant_reduce_requant_split", "zpp_dequant_reduce_average",
-            "zpp_status_string", "zpp_abi_version")
+            "zpp_set_pointer_checks", "zpp_status_string", "zpp_abi_version")
 
 
 class ZppError(RuntimeError):
@@ -74,6 +74,8 @@ def _load() -> ctypes.CDLL:
         f = getattr(lib, name)
         f.argtypes = args
         f.restype = ctypes.c_int
+    lib.zpp_set_pointer_checks.argtypes = [ctypes.c_int32]
+    lib.zpp_set_pointer_checks.restype = ctypes.c_int32
     lib.zpp_status_string.argtypes = [ctypes.c_int]
     lib.zpp_status_string.restype = ctypes.c_char_p
     lib.zpp_abi_version.argtypes = []
@@ -154,6 +156,12 @@ def zpp_dequant_reduce_average(codes_in, codes_stride_bytes, scales_in, scales_s
                                block, divisor, avg_out, stream=None) -> None:
     _call("zpp_dequant_reduce_average", _ptr(codes_in), codes_stride_bytes, _ptr(scales_in), scales_stride,
           n_inputs, bits_in, numel, block, divisor, _ptr(avg_out), _stream(stream))
+
+
+def zpp_set_pointer_checks(enabled: bool) -> bool:
+    """Switch the library's HIP-runtime pointer and range checks on or off for
+    the process (see include/zpp.h); returns the previous setting."""
+    return bool(_lib.zpp_set_pointer_checks(1 if enabled else 0))
 
 
 def zpp_status_string(status: int) -> str:

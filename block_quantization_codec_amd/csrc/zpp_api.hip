@@ -4,7 +4,8 @@
 // GPU: pure argument checks first (null pointers, sizes, block, bit widths,
 // alignment, overlapping outputs), then checks with the HIP runtime that
 // every pointer is memory the GPU can address and that each buffer's whole
-// byte range lies inside its allocation. Only then is a kernel launched on
+// byte range lies inside its allocation (unless the caller has switched
+// those off with zpp_set_pointer_checks). Only then is a kernel launched on
 // the caller's stream. Any failure returns a status code with nothing
 // launched and every output untouched.
 #include <atomic>
@@ -86,53 +87,82 @@ bool overlap(Range a, Range b) {
     return a0 < b0 + static_cast<uintptr_t>(b.bytes) && b0 < a0 + static_cast<uintptr_t>(a.bytes);
 }
 
-// The pointer must be device-addressable and [p, p + bytes) must lie in one allocation.
-zpp_status check_device_range(Range r) {
-    if (r.bytes <= 0) return ZPP_OK;
-    hipPointerAttribute_t attr;
-    hipError_t e = hipPointerGetAttributes(&attr, r.p);
-    if (e != hipSuccess) {
-        (void)hipGetLastError();
-        return ZPP_ERR_POINTER;
+// Whether calls query the HIP runtime about their pointers (see
+// zpp_set_pointer_checks); the pure argument checks always run.
+std::atomic<int> g_pointer_checks{1};
+
+// The HIP-runtime checks of one call: every pointer must be memory the
+// current GPU can address, and [p, p + bytes) must lie in one allocation.
+// The current device is queried once per call, and a buffer inside an
+// allocation already validated in this call needs no further queries (its
+// memory type and device are the allocation's).
+class PointerChecks {
+  public:
+    template <size_t N>
+    zpp_status all(const Range (&rs)[N]) {
+        if (g_pointer_checks.load(std::memory_order_relaxed) == 0) return ZPP_OK;
+        for (const Range &r : rs) {
+            const zpp_status s = one(r);
+            if (s != ZPP_OK) return s;
+        }
+        return ZPP_OK;
     }
-    if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged && attr.type != hipMemoryTypeHost &&
-        attr.type != hipMemoryTypeUnified)
-        return ZPP_ERR_POINTER;
-    if (attr.type == hipMemoryTypeHost && attr.devicePointer == nullptr) return ZPP_ERR_POINTER;
-    if (attr.type == hipMemoryTypeDevice) {  // another GPU's memory needs peer access from this one
-        int cur = 0;
-        if (hipGetDevice(&cur) != hipSuccess) {
+
+  private:
+    struct Alloc {
+        uintptr_t b0, b1;
+    };
+    Alloc seen_[8];
+    int n_seen_ = 0;
+    int dev_ = -1;
+
+    zpp_status one(Range r) {
+        if (r.bytes <= 0) return ZPP_OK;
+        const uintptr_t p0 = reinterpret_cast<uintptr_t>(r.p);
+        const uintptr_t p1 = p0 + static_cast<uintptr_t>(r.bytes);
+        for (int i = 0; i < n_seen_; ++i)
+            if (seen_[i].b0 <= p0 && p1 <= seen_[i].b1) return ZPP_OK;
+        hipPointerAttribute_t attr;
+        hipError_t e = hipPointerGetAttributes(&attr, r.p);
+        if (e != hipSuccess) {
             (void)hipGetLastError();
             return ZPP_ERR_POINTER;
         }
-        if (attr.device != cur) {
-            int can = 0;
-            if (hipDeviceCanAccessPeer(&can, cur, attr.device) != hipSuccess || !can) {
+        if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged && attr.type != hipMemoryTypeHost &&
+            attr.type != hipMemoryTypeUnified)
+            return ZPP_ERR_POINTER;
+        if (attr.type == hipMemoryTypeHost && attr.devicePointer == nullptr) return ZPP_ERR_POINTER;
+        if (attr.type == hipMemoryTypeDevice) {  // another GPU's memory needs peer access from this one
+            if (dev_ < 0 && hipGetDevice(&dev_) != hipSuccess) {
                 (void)hipGetLastError();
+                dev_ = -1;
                 return ZPP_ERR_POINTER;
             }
+            if (attr.device != dev_) {
+                int can = 0;
+                if (hipDeviceCanAccessPeer(&can, dev_, attr.device) != hipSuccess || !can) {
+                    (void)hipGetLastError();
+                    return ZPP_ERR_POINTER;
+                }
+            }
         }
+        hipDeviceptr_t base = nullptr;
+        size_t size = 0;
+        e = hipMemGetAddressRange(&base, &size, const_cast<void *>(r.p));
+        if (e == hipSuccess && base != nullptr && size > 0) {
+            const uintptr_t b0 = reinterpret_cast<uintptr_t>(base);
+            if (p0 < b0 || p1 > b0 + size) return ZPP_ERR_ARG;
+            if (n_seen_ < 8) seen_[n_seen_++] = Alloc{b0, b0 + size};
+        } else {
+            (void)hipGetLastError();
+        }
+        return ZPP_OK;
     }
-    hipDeviceptr_t base = nullptr;
-    size_t size = 0;
-    e = hipMemGetAddressRange(&base, &size, const_cast<void *>(r.p));
-    if (e == hipSuccess && base != nullptr && size > 0) {
-        const uintptr_t b0 = reinterpret_cast<uintptr_t>(base);
-        const uintptr_t p0 = reinterpret_cast<uintptr_t>(r.p);
-        if (p0 < b0 || p0 + static_cast<uintptr_t>(r.bytes) > b0 + size) return ZPP_ERR_ARG;
-    } else {
-        (void)hipGetLastError();
-    }
-    return ZPP_OK;
-}
+};
 
 template <size_t N>
 zpp_status check_all(const Range (&rs)[N]) {
-    for (const Range &r : rs) {
-        const zpp_status s = check_device_range(r);
-        if (s != ZPP_OK) return s;
-    }
-    return ZPP_OK;
+    return PointerChecks().all(rs);
 }
 
 // A triple-chevron launch reports failure only through the thread's pending
@@ -338,6 +368,10 @@ zpp_status zpp_dequant_reduce_average(const void *codes_in, int64_t codes_stride
         return zpp::launch_drr_average(codes_in, codes_stride_bytes, scales_in, scales_stride, n_inputs, bits_in,
                    numel, log2_of(block), divisor, avg_out, static_cast<hipStream_t>(stream));
     });
+}
+
+int32_t zpp_set_pointer_checks(int32_t enabled) {
+    return g_pointer_checks.exchange(enabled != 0 ? 1 : 0, std::memory_order_relaxed);
 }
 
 const char *zpp_status_string(int32_t status) {

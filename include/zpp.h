@@ -271,6 +271,23 @@ zpp_status zpp_dequant_reduce_average(const void *codes_in, int64_t codes_stride
                                       int32_t n_inputs, int32_t bits_in, int64_t numel,
                                       int32_t block, int32_t divisor, float *avg_out, void *stream);
 
+/*
+ * Switch the library's HIP-runtime pointer checks on (enabled != 0, the
+ * default) or off for the whole process; returns the previous setting (1 or
+ * 0). With the checks on, every call asks the HIP runtime, before it
+ * launches anything, whether each pointer is memory the current GPU can
+ * address (ZPP_ERR_POINTER otherwise) and whether each buffer's byte range
+ * lies inside its allocation (ZPP_ERR_ARG otherwise), about 0.2 us of host
+ * time per buffer. With them off, those two checks are skipped: the caller
+ * guarantees that every pointer it passes is device-addressable and that
+ * every buffer is as long as the call's sizes imply, and a call that breaks
+ * this faults the GPU instead of returning an error. Every other check (NULL
+ * pointers, sizes, block, bit widths, strides, alignment, overlapping
+ * outputs) always runs. Safe to call from any thread; calls already past
+ * their checks are not affected.
+ */
+int32_t zpp_set_pointer_checks(int32_t enabled);
+
 /* Static, human-readable name of a status code (a zpp_status value); any
  * other value gives "unknown zpp_status". Never NULL. */
 const char *zpp_status_string(int32_t status);

@@ -70,6 +70,15 @@ def test_abi_version_and_status_strings(z):
         assert z.zpp_status_string(bad) == "unknown zpp_status"
 
 
+def test_pointer_check_switch_returns_the_previous_setting(z):
+    """zpp_set_pointer_checks touches no GPU: it only swaps the setting."""
+    f = z.library().zpp_set_pointer_checks
+    assert f(0) == 1
+    assert f(7) == 0          # any non-zero value switches them on
+    assert f(1) == 1
+    assert z.zpp_set_pointer_checks(True) is True
+
+
 def test_status_values_match_the_header(z):
     """The numeric status codes: 0-5 as the boundary contract fixes them
     (OK, NULL, ARG, ALIGN, UNSUPPORTED, LAUNCH), the two extra argument

@@ -7,7 +7,10 @@ byte range runs past its allocation (ZPP_ERR_ARG), misaligned pointers
 (ZPP_ERR_ALIGN) and overlapping buffers (ZPP_ERR_OVERLAP). Pinned host
 memory, which the GPU can address, is accepted as input and gives the same
 result as device memory. A HIP error left pending by an unrelated earlier
-call does not make a good call fail.
+call does not make a good call fail. Buffers carved from one allocation are
+checked against it (a range that starts inside but runs past it is still
+refused), and with the HIP-runtime pointer checks switched off the pure
+argument checks still report.
 """
 from __future__ import annotations
 
@@ -131,3 +134,70 @@ def test_pending_hip_error_does_not_fail_a_good_call():
     oc, os_ = oracle.quantize(x, B, 8)
     assert_bits_equal(host(c), oc, "codes after a pending error")
     assert_bits_equal(host(s), os_, "scales after a pending error")
+
+
+def test_buffers_carved_from_one_allocation():
+    """Input and outputs carved out of one device allocation, as torch's
+    caching allocator hands them out: the allocation is looked up once and
+    the later buffers inside it are accepted; the result matches the oracle
+    and the bytes between the buffers stay untouched."""
+    z = _z()
+    n, B = 4096, 256
+    x = synth.small_bf16(n, (0, 506), 0.02, 1e-3, 50.0)
+    arena = torch.full((3 * 16384,), 0xA5, dtype=torch.uint8, device="cuda")
+    arena[:2 * n].copy_(torch.from_numpy(x.view(np.uint8)).cuda())
+    base = arena.data_ptr()
+    z.zpp_quantize_blocks(base, z.ZPP_BF16, n, B, 8, base + 16384, base + 32768)
+    torch.cuda.synchronize()
+    a = host(arena)
+    oc, os_ = oracle.quantize(x, B, 8)
+    assert_bits_equal(a[16384:16384 + n], oc, "codes")
+    assert_bits_equal(a[32768:32768 + 4 * n // B].view(np.float32), os_, "scales")
+    assert np.all(a[2 * n:16384] == 0xA5) and np.all(a[16384 + n:32768] == 0xA5)
+    assert np.all(a[32768 + 4 * n // B:] == 0xA5)
+
+
+def test_range_starting_in_a_checked_allocation_but_running_past_it():
+    """The codes are found inside their allocation; the scales start in the
+    same allocation but their stride carries the second input a gigabyte past
+    its end: still ZPP_ERR_ARG, nothing written."""
+    z = _z()
+    n, B = 1024, 256
+    bufs = [Guarded(8192) for _ in range(3)]
+    bufs.sort(key=lambda g: g.ptr)
+    gc, gs, arena = bufs  # the inputs' allocation is the highest, so the claimed range overlaps no output
+    _expect_status(z.ZPP_ERR_ARG,
+                   lambda: z.zpp_dequant_reduce_requant(arena.ptr, 0, arena.ptr + 4096, 1 << 28, 2, 8, n, B, gc.ptr,
+                                                        gs.ptr, 8, None), gc, gs)
+
+
+def test_pointer_checks_switched_off():
+    """With the HIP-runtime pointer checks off, valid calls give the same
+    result and every pure argument check still reports; switched back on,
+    host memory is refused again. (Only valid pointers are passed while the
+    checks are off: an invalid one would reach the GPU.)"""
+    z = _z()
+    n, B = 4096, 256
+    x = synth.small_bf16(n, (0, 507), 0.02, 1e-3, 50.0)
+    xd = dev(x)
+    gc, gs = Guarded(n + 64), Guarded(4 * n // B + 64)
+    assert z.zpp_set_pointer_checks(False) is True
+    try:
+        c = torch.empty(n, dtype=torch.uint8, device="cuda")
+        s = torch.empty(n // B, dtype=torch.float32, device="cuda")
+        z.zpp_quantize_blocks(xd, z.ZPP_BF16, n, B, 8, c, s)
+        torch.cuda.synchronize()
+        oc, os_ = oracle.quantize(x, B, 8)
+        assert_bits_equal(host(c), oc, "codes, checks off")
+        assert_bits_equal(host(s), os_, "scales, checks off")
+        _expect_status(z.ZPP_ERR_ALIGN, lambda: z.zpp_quantize_blocks(xd, z.ZPP_BF16, n, B, 8, gc.ptr + 8, gs.ptr),
+                       gc, gs)
+        _expect_status(z.ZPP_ERR_OVERLAP,
+                       lambda: z.zpp_quantize_blocks(xd, z.ZPP_BF16, n, B, 8, gc.ptr, gc.ptr + 64), gc)
+        _expect_status(z.ZPP_ERR_NULL, lambda: z.zpp_quantize_blocks(xd, z.ZPP_BF16, n, B, 8, None, gs.ptr), gs)
+        assert z.zpp_set_pointer_checks(False) is False
+    finally:
+        z.zpp_set_pointer_checks(True)
+    host_buf = np.zeros(2 * n, np.uint8)
+    _expect_status(z.ZPP_ERR_POINTER,
+                   lambda: z.zpp_quantize_blocks(host_buf.ctypes.data, z.ZPP_BF16, n, B, 8, gc.ptr, gs.ptr), gc, gs)
