@@ -29,7 +29,7 @@ __global__ __launch_bounds__(kBlockThreads) void dequantize_kernel(const uint8_t
                                                                    const float *__restrict__ scales, int64_t numel,
                                                                    int log2b, uint8_t *__restrict__ y) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t wave = xcd_block(blockIdx.x, gridDim.x) * (kBlockThreads / kWave) + (threadIdx.x / kWave);
+    const int64_t wave = xcd_block(blockIdx.x, gridDim.x) * (kBlockThreads / kWave) + wave_in_block();
     const int64_t n_waves = static_cast<int64_t>(gridDim.x) * (kBlockThreads / kWave);
 
     for (int64_t t0 = wave * kTile; t0 < numel; t0 += n_waves * kTile) {

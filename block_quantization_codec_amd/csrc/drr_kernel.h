@@ -584,8 +584,8 @@ __attribute__((amdgpu_waves_per_eu(drr_min_waves<BITS_IN, LOG2B, E>(), 8))) void
     constexpr int U = G::U;
 
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = static_cast<int>(xcd_block(blockIdx.x, gridDim.x)) * (kBlockThreads / kWave) +
-                     static_cast<int>(threadIdx.x / kWave);
+    const int wib = wave_in_block();
+    const int wave = static_cast<int>(xcd_block(blockIdx.x, gridDim.x)) * (kBlockThreads / kWave) + wib;
     const int n_waves = static_cast<int>(gridDim.x) * (kBlockThreads / kWave);
 
     for (int64_t t0 = static_cast<int64_t>(wave) * G::TILE; t0 < numel;
@@ -622,7 +622,7 @@ __attribute__((amdgpu_waves_per_eu(drr_min_waves<BITS_IN, LOG2B, E>(), 8))) void
         } else if constexpr (ZPP_DRR_LDS && G::U == 1 && G::ND == 4) {
             __shared__ uint32_t lds_codes[kBlockThreads / kWave][G::RB][kWave][4];  // 8 KB per wave
             consume_lds<G, G::RB>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, o, acc,
-                                  lds_codes[threadIdx.x / kWave], lane);
+                                  lds_codes[wib], lane);
         } else {
             consume_padded<G, G::RB>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, o, acc);
         }

@@ -168,7 +168,7 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_kernel(const uint8_t *
         scales += static_cast<int64_t>(blockIdx.y) * (numel >> LOG2B);
     }
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave_in_group = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int wave_in_group = wave_in_block();
     const int64_t wave = xcd_block(blockIdx.x, gridDim.x) * (kBlockThreads / kWave) + wave_in_group;
     const int64_t n_waves = static_cast<int64_t>(gridDim.x) * (kBlockThreads / kWave);
 

@@ -227,6 +227,13 @@ __device__ __forceinline__ int32_t code_at(uint32_t w, int i) {
 
 // ---- launch geometry --------------------------------------------------------
 
+// This wave's index within its workgroup, as a value the compiler knows to be
+// the same in every lane: loops and addresses derived from it stay in scalar
+// registers and branches on it are uniform.
+__device__ __forceinline__ int wave_in_block() {
+    return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave));
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2).
 // Renumbering them so that each XCD takes one contiguous run of the grid keeps
 // neighbouring tiles, which share cache lines of the small scale arrays, in

@@ -3,7 +3,7 @@
 The library keeps no per-call state and allocates nothing, so a sequence of
 its calls can be captured once and replayed, and calls on different streams
 can run at the same time. Graph test: the qgZ chain (reorder fused into the
-4-bit quantize, hop 1, hop 2 sum and average) and the 8-bit round trip are
+4-bit quantize, hop 1 whole and split, hop 2 sum and average) and the 8-bit round trip are
 captured into one graph, then replayed three times. Between replays the
 program does its own eager work (it rewrites the inputs) and synchronizes,
 and every replay must equal an eager run on the same inputs bit for bit.
@@ -51,6 +51,10 @@ class Chain:
         C = n * self.S
         self.h1c = torch.empty(C // 2, dtype=torch.uint8, device="cuda")
         self.h1s = torch.empty(C // B, dtype=torch.float32, device="cuda")
+        self.sc = torch.empty((C - self.S) // 2, dtype=torch.uint8, device="cuda")  # split hop 1: sent part
+        self.ss = torch.empty((C - self.S) // B, dtype=torch.float32, device="cuda")
+        self.kc = torch.empty(self.S // 2, dtype=torch.uint8, device="cuda")        # and kept sub-chunk 1
+        self.ks = torch.empty(self.S // B, dtype=torch.float32, device="cuda")
         self.sum = torch.empty(self.S, dtype=torch.float32, device="cuda")
         self.avg = torch.empty(self.S, dtype=torch.float32, device="cuda")
         self.wc = torch.empty(self.w.numel(), dtype=torch.uint8, device="cuda")
@@ -65,6 +69,8 @@ class Chain:
         # hop 1 as local rank 0 of node 0 would run it: the g chunks 0 of the
         # reordered buffer stand in for the g local ranks' contributions
         z.zpp_dequant_reduce_requant(self.qc, 0, self.qs, 0, g, 4, C, B, self.h1c, self.h1s, 4, None)
+        z.zpp_dequant_reduce_requant_split(self.qc, 0, self.qs, 0, g, 4, C, B, S, S, self.sc, self.ss, self.kc,
+                                           self.ks, 4)
         z.zpp_dequant_reduce_requant(self.h1c, S // 2, self.h1s, S // B, n, 4, S, B, None, None, 0, self.sum)
         z.zpp_dequant_reduce_average(self.h1c, S // 2, self.h1s, S // B, n, 4, S, B, n * g, self.avg)
         z.zpp_quantize_blocks(self.w, z.ZPP_BF16, self.w.numel(), 256, 8, self.wc, self.ws)
@@ -72,10 +78,11 @@ class Chain:
 
     def outputs(self):
         return [host(t).copy() for t in (self.qc, self.qs, self.h1c, self.h1s, self.sum, self.avg, self.wc,
-                                         self.ws, self.wy)]
+                                         self.ws, self.wy, self.sc, self.ss, self.kc, self.ks)]
 
     def clear(self):
-        for t in (self.qc, self.qs, self.h1c, self.h1s, self.sum, self.avg, self.wc, self.ws, self.wy):
+        for t in (self.qc, self.qs, self.h1c, self.h1s, self.sum, self.avg, self.wc, self.ws, self.wy, self.sc,
+                  self.ss, self.kc, self.ks):
             t.view(torch.uint8).fill_(0xA5)
 
 
@@ -92,7 +99,8 @@ def test_graph_replays_equal_eager_runs():
         ch.launch()
     torch.cuda.synchronize()
     names = ["codes", "scales", "hop-1 codes", "hop-1 scales", "hop-2 sum", "hop-2 average", "int8 codes",
-             "int8 scales", "bf16 dequantized"]
+             "int8 scales", "bf16 dequantized", "split hop-1 sent codes", "split hop-1 sent scales",
+             "split hop-1 kept codes", "split hop-1 kept scales"]
     for rep, factor in enumerate((1.0, 2.0, 0.25)):
         if factor != 1.0:  # the program's own eager work between replays: new inputs
             ch.grad.mul_(factor)

@@ -162,6 +162,31 @@ def test_random_hop_reduce_and_average(seed):
         assert gc.untouched() and gs.untouched()
         assert_bits_equal(gs.as_np(np.float32), so, f"requantized scales seed={seed}")
         assert_bits_equal(gc.bytes(), co, f"requantized codes seed={seed}")
+    if bits_out and finite:  # the same hop with its output split at a random kept window of blocks
+        nb = n // B
+        k0 = int(rng.integers(0, nb + 1))
+        kl = int(rng.integers(0, nb - k0 + 1))
+        k0, kl = k0 * B, kl * B
+        gsc = Guarded((n - kl) * bits_out // 8) if n > kl else None
+        gss = Guarded(4 * ((n - kl) // B)) if n > kl else None
+        gkc = Guarded(kl * bits_out // 8) if kl else None
+        gks = Guarded(4 * (kl // B)) if kl else None
+        torch.cuda.synchronize()
+        z.zpp_dequant_reduce_requant_split(cd, per_c, sd, per_s, R, bits_in, n, B, k0, kl,
+                                           gsc.ptr if gsc else None, gss.ptr if gss else None,
+                                           gkc.ptr if gkc else None, gks.ptr if gks else None, bits_out)
+        torch.cuda.synchronize()
+        cb = bits_out // 8 if bits_out == 8 else 0.5
+        c0, c1 = int(k0 * cb), int((k0 + kl) * cb)
+        if kl:
+            assert gkc.untouched() and gks.untouched()
+            assert_bits_equal(gkc.bytes(), co[c0:c1], f"split kept codes seed={seed}")
+            assert_bits_equal(gks.as_np(np.float32), so[k0 // B:(k0 + kl) // B], f"split kept scales seed={seed}")
+        if n > kl:
+            assert gsc.untouched() and gss.untouched()
+            assert_bits_equal(gsc.bytes(), np.concatenate([co[:c0], co[c1:]]), f"split sent codes seed={seed}")
+            assert_bits_equal(gss.as_np(np.float32), np.concatenate([so[:k0 // B], so[(k0 + kl) // B:]]),
+                              f"split sent scales seed={seed}")
     divisor = int(rng.choice([1, 3, 7, 8, 96, 1 << 20]))
     ga = Guarded(4 * n)
     torch.cuda.synchronize()
