@@ -399,6 +399,31 @@ __device__ __forceinline__ void consume_overlapped(const uint8_t *__restrict__ c
 // to that register budget), which keeps more loads in flight while other
 // waves sum and requantize.
 
+// Word 3 of a raw buffer resource (no swizzle, no index stride) on this GPU
+// family: the data-format field set to 32 bits, which untyped loads need to
+// be served at all.
+constexpr int kRawBufferConfig = 0x00020000;
+
+// A buffer resource over one input's bytes of this launch: a wave-uniform
+// base and size in scalar registers. Loads through it take a 32-bit lane
+// offset, so no lane computes a 64-bit address per input, and a load past
+// `bytes` returns zeros instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t input_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                             kRawBufferConfig);
+}
+
+// One binary32 at byte offset `off` of a buffer.
+__device__ __forceinline__ float buffer_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return as_f(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+// 16 bytes per lane at byte offset `off` of a buffer, straight into LDS at
+// `dst` (lane i's bytes at dst + 16 i).
+__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t r, uint32_t off, void *dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, off, 0, 0, 0);
+}
+
 // Wait until at most N of this wave's vector-memory operations are
 // outstanding. The compiler does not track loads into LDS, so their readers
 // wait here explicitly; the clobber keeps memory accesses on their side.
@@ -449,9 +474,12 @@ __device__ __forceinline__ void sum_from_lds(const uint32_t (*slot)[kWave][4], c
 template <typename G, int NB>
 __device__ __forceinline__ void consume_lds(const uint8_t *__restrict__ codes_in, int64_t codes_stride,
                                             const float *__restrict__ scales_in, int64_t scales_stride,
-                                            int n_inputs, const LaneOffsets<G> &o, float (&acc)[G::U][G::E],
-                                            uint32_t (*slot)[kWave][4], int lane) {
+                                            int n_inputs, int numel, const LaneOffsets<G> &o,
+                                            float (&acc)[G::U][G::E], uint32_t (*slot)[kWave][4], int lane) {
     static_assert(G::U == 1 && G::ND == 4, "one 16-byte code vector per input and lane");
+    // bytes of one input within this launch (numel < 2^30)
+    const uint32_t code_bytes = static_cast<uint32_t>(numel) / 2u;
+    const uint32_t scale_bytes = (static_cast<uint32_t>(numel) >> G::LOG2B) * 4u;
     for (int r0 = 0; r0 < n_inputs; r0 += NB) {
         // the previous batch's reads of the slots are complete before they are refilled
         if (r0 > 0) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -459,9 +487,9 @@ __device__ __forceinline__ void consume_lds(const uint8_t *__restrict__ codes_in
 #pragma unroll
         for (int k = 0; k < NB; ++k) {
             const int ri = min(r0 + k, n_inputs - 1);
-            const uint8_t *sc = reinterpret_cast<const uint8_t *>(scales_in + static_cast<int64_t>(ri) * scales_stride);
+            const __amdgpu_buffer_rsrc_t rs = input_rsrc(scales_in + static_cast<int64_t>(ri) * scales_stride, scale_bytes);
 #pragma unroll
-            for (int u = 0; u < G::U; ++u) s[k][u] = *reinterpret_cast<const float *>(sc + o.scale[u]);
+            for (int u = 0; u < G::U; ++u) s[k][u] = buffer_f32(rs, o.scale[u]);
         }
         // The batch's choice of product formula (see add_batch). Taking it
         // here makes the compiler wait for the scales before the loads into
@@ -471,12 +499,10 @@ __device__ __forceinline__ void consume_lds(const uint8_t *__restrict__ codes_in
 #pragma unroll
         for (int k = 0; k < NB; ++k) {
             const int ri = min(r0 + k, n_inputs - 1);
-            const uint8_t *c = codes_in + static_cast<int64_t>(ri) * codes_stride;
+            const __amdgpu_buffer_rsrc_t rc = input_rsrc(codes_in + static_cast<int64_t>(ri) * codes_stride, code_bytes);
 #pragma unroll
             for (int u = 0; u < G::U; ++u)
-                __builtin_amdgcn_global_load_lds(static_cast<const void *>(c + o.code[u]),
-                                                 (__attribute__((address_space(3))) void *)(&slot[k * G::U + u][0][0]),
-                                                 16, 0, 0);
+                buffer_to_lds16(rc, o.code[u], &slot[k * G::U + u][0][0]);
         }
         __builtin_amdgcn_sched_barrier(0);
         sum_from_lds<G, NB>(slot, s, lane, acc, r0 == 0, n_inputs - r0, fast);
@@ -518,7 +544,7 @@ struct DrrOut {
 // stored; then the sums requantized per block and stored.
 template <typename G, int BITS_OUT, bool AVG>
 __device__ __forceinline__ void finish_tile(float (&acc)[G::U][G::E], const bool (&ok)[G::U],
-                                            const uint32_t (&e)[G::U], int lane, const DrrOut &out) {
+                                            const uint32_t (&e)[G::U], uint32_t tb, int lane, const DrrOut &out) {
     static_assert(!AVG || BITS_OUT == 0, "the average is a final binary32 output");
     constexpr int U = G::U, E = G::E;
     if (AVG || out.sum_out != nullptr) {
@@ -561,14 +587,30 @@ __device__ __forceinline__ void finish_tile(float (&acc)[G::U][G::E], const bool
             uint32_t cw[E * BITS_OUT / 32];
             pack_codes<E, BITS_OUT>(mg, cw);
             if (!ok[u]) continue;
-            // output position: inside the keep window, or in the rest with the window left out
-            const uint32_t rel = e[u] - out.kb;
-            const bool keep = rel < out.klen;
-            const uint32_t idx = keep ? rel : (e[u] < out.kb ? e[u] : e[u] - out.klen);
-            uint8_t *cdst = keep ? out.codes_keep : out.codes_out;
-            float *sdst = keep ? out.scales_keep : out.scales_out;
-            store_dwords<E * BITS_OUT / 32>(cdst + idx * BITS_OUT / 8, cw);
-            if (u == 0 && (lane & (G::L - 1)) == 0) sdst[idx >> G::LOG2B] = sc;
+            // Output position: inside the keep window, or in the rest with the
+            // window left out. The window is whole blocks, so a tile lies
+            // before it, after it or inside it, decided once for the wave,
+            // except for at most two tiles per launch that hold one of its
+            // ends, whose lanes decide each for itself.
+            const uint32_t k1 = out.kb + out.klen;
+            const uint32_t te = tb + G::TILE;
+            const bool inside = out.klen != 0 && tb >= out.kb && te <= k1;
+            const bool after = out.klen != 0 && tb >= k1;
+            if (out.klen == 0 || te <= out.kb || after || inside) {
+                const uint32_t idx = e[u] - (inside ? out.kb : (after ? out.klen : 0u));
+                uint8_t *cdst = inside ? out.codes_keep : out.codes_out;
+                float *sdst = inside ? out.scales_keep : out.scales_out;
+                store_dwords<E * BITS_OUT / 32>(cdst + idx * BITS_OUT / 8, cw);
+                if (u == 0 && (lane & (G::L - 1)) == 0) sdst[idx >> G::LOG2B] = sc;
+            } else {
+                const uint32_t rel = e[u] - out.kb;
+                const bool keep = rel < out.klen;
+                const uint32_t idx = keep ? rel : (e[u] < out.kb ? e[u] : e[u] - out.klen);
+                uint8_t *cdst = keep ? out.codes_keep : out.codes_out;
+                float *sdst = keep ? out.scales_keep : out.scales_out;
+                store_dwords<E * BITS_OUT / 32>(cdst + idx * BITS_OUT / 8, cw);
+                if (u == 0 && (lane & (G::L - 1)) == 0) sdst[idx >> G::LOG2B] = sc;
+            }
         }
     }
 }
@@ -588,16 +630,18 @@ __attribute__((amdgpu_waves_per_eu(drr_min_waves<BITS_IN, LOG2B, E>(), 8))) void
     const int wave = static_cast<int>(xcd_block(blockIdx.x, gridDim.x)) * (kBlockThreads / kWave) + wib;
     const int n_waves = static_cast<int>(gridDim.x) * (kBlockThreads / kWave);
 
-    for (int64_t t0 = static_cast<int64_t>(wave) * G::TILE; t0 < numel;
-         t0 += static_cast<int64_t>(n_waves) * G::TILE) {
+    // A launch covers at most 2^29 elements: tile offsets, and the grid
+    // stride added to them, fit in 32 bits.
+    const uint32_t n = static_cast<uint32_t>(numel);
+    for (uint32_t t0 = static_cast<uint32_t>(wave) * G::TILE; t0 < n; t0 += static_cast<uint32_t>(n_waves) * G::TILE) {
         uint32_t e[U];
         bool ok[U];
         LaneOffsets<G> o;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t e0 = t0 + static_cast<int64_t>(u) * G::SEG + lane * E;
-            ok[u] = e0 < numel;
-            e[u] = ok[u] ? static_cast<uint32_t>(e0) : 0u;
+            const uint32_t e0 = t0 + static_cast<uint32_t>(u * G::SEG + lane * E);
+            ok[u] = e0 < n;
+            e[u] = ok[u] ? e0 : 0u;
             o.code[u] = e[u] * BITS_IN / 8;
             o.scale[u] = (e[u] >> LOG2B) * 4u;
         }
@@ -621,12 +665,12 @@ __attribute__((amdgpu_waves_per_eu(drr_min_waves<BITS_IN, LOG2B, E>(), 8))) void
             consume<G, 1>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, o, r, acc);
         } else if constexpr (ZPP_DRR_LDS && G::U == 1 && G::ND == 4) {
             __shared__ uint32_t lds_codes[kBlockThreads / kWave][G::RB][kWave][4];  // 8 KB per wave
-            consume_lds<G, G::RB>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, o, acc,
+            consume_lds<G, G::RB>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, numel, o, acc,
                                   lds_codes[wib], lane);
         } else {
             consume_padded<G, G::RB>(codes_in, codes_stride, scales_in, scales_stride, n_inputs, o, acc);
         }
-        finish_tile<G, BITS_OUT, AVG>(acc, ok, e, lane, out);
+        finish_tile<G, BITS_OUT, AVG>(acc, ok, e, t0, lane, out);
     }
 }
 
