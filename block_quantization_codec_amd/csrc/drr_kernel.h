@@ -392,12 +392,13 @@ __device__ __forceinline__ void consume_overlapped(const uint8_t *__restrict__ c
 //
 // With 4-bit inputs a lane's codes of one input are one 16-byte vector. The
 // batch's scales are loaded into registers as elsewhere; each code vector
-// then goes straight from memory into this wave's own LDS slot
-// (global_load_lds_dwordx4: a kilobyte per instruction, no registers held
-// while it is in flight), and is read back just before it is summed. The
-// registers saved let 5 waves share a SIMD instead of 4 (the kernel is held
-// to that register budget), which keeps more loads in flight while other
-// waves sum and requantize.
+// then goes straight from memory into this wave's own LDS slot (a buffer
+// load into LDS: a kilobyte per instruction, no registers held while it is
+// in flight), and is read back just before it is summed. The registers
+// saved let 5 waves share a SIMD instead of 4 (the kernel is held to that
+// register budget), which keeps more loads in flight while other waves sum
+// and requantize. Both kinds of load address an input through a buffer
+// resource, so the per-input address work is scalar.
 
 // Word 3 of a raw buffer resource (no swizzle, no index stride) on this GPU
 // family: the data-format field set to 32 bits, which untyped loads need to
