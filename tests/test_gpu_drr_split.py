@@ -95,11 +95,20 @@ WIDE = 4096 * 2048 + 7 * 256
 
 
 @pytest.mark.parametrize("numel", [SMALL, WIDE])
-@pytest.mark.parametrize("where", ["start", "middle", "end", "none", "all"])
+@pytest.mark.parametrize("where", ["start", "middle", "end", "none", "all", "tile_ends", "within_one_tile"])
 def test_window_positions(numel, where):
+    """Tiles are 512 elements in the 8-element layout (SMALL) and 2048 in the
+    32-element one (WIDE). A tile lies before, after or inside the window,
+    or holds one or both of its ends; "tile_ends" puts both ends on tile
+    boundaries (no tile holds an end), "within_one_tile" both ends inside
+    the same tile (with 2-block tiles: one block, from mid-tile to the
+    tile's end)."""
     B = 256
+    tile = 512 if numel == SMALL else 2048
     w = {"start": (0, 31 * B), "middle": (numel // 2 // B * B, 5 * B), "end": (numel - 9 * B, 9 * B),
-         "none": (numel // B // 3 * B, 0), "all": (0, numel)}[where]
+         "none": (numel // B // 3 * B, 0), "all": (0, numel),
+         "tile_ends": (numel // 2 // tile * tile, 4 * tile),
+         "within_one_tile": (numel // 3 // tile * tile + B, max(tile - 2 * B, B))}[where]
     _split(8, 4, 4, numel, B, *w)
 
 
