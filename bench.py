@@ -30,8 +30,11 @@ reported beside them: the unfused pair (standalone reorder of the bf16
 bucket, then quantize of the reordered buffer), the other unfused order
 (quantize the bucket as it is, then reorder its codes and scales), and hop 2
 writing the averaged shard, a plain 1 GiB device copy (the slice reorder
-with one slice) that each row is also compared with (`copy_frac`), and the
-step captured into a HIP graph and replayed (`graph_step`). The CPU baseline
+with one slice) that each row is also compared with (`copy_frac`), for rows
+moving less than 1 GiB a plain copy of the row's own read + write bytes with
+its buffers rotated over 1 GiB (`of_copy_same_size`: how close the row comes
+to what a copy of its size reaches, launch and ramp included), and the step
+captured into a HIP graph and replayed (`graph_step`). The CPU baseline
 runs the plain C oracle over the same work as one step (the reorder and the
 quantize as two oracle steps), once on one core and twice on every core the
 process may use (independent block ranges on a thread pool).
@@ -348,6 +351,37 @@ def copy_ceiling(torch, z, stream, K):
             "bytes": 2 * n, "ms": round(ms, 5), "GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
 
 
+_SAME_SIZE_COPY = {}
+
+
+def same_size_copy(torch, z, stream, rw_bytes: int, K: int) -> float:
+    """Mean HIP-event time (ms) of a plain device copy that reads and writes
+    as many bytes as a row does (rw_bytes in total), through the library's
+    one-slice reorder, with sources and destinations rotated over at least
+    1 GiB so every launch reads from HBM: the rate a kernel of that size can
+    reach, launch and ramp included, against which the small rows are read."""
+    import math
+    half = max(4096, (rw_bytes // 2 + 4095) // 4096 * 4096)
+    if half in _SAME_SIZE_COPY:
+        return _SAME_SIZE_COPY[half]
+    ncopy = max(2, math.ceil(ROTATE_BYTES / (2 * half)))
+    src = [torch.zeros(half, dtype=torch.uint8, device="cuda") for _ in range(ncopy)]
+    dst = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in range(ncopy)]
+    for k in range(ncopy):
+        z.zpp_reorder_slices(src[k], dst[k], half, 1, 1)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    for k, (a, b) in enumerate(ev):
+        a.record(stream)
+        z.zpp_reorder_slices(src[(k + 1) % ncopy], dst[(k + 1) % ncopy], half, 1, 1)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / K
+    del src, dst
+    _SAME_SIZE_COPY[half] = ms
+    return ms
+
+
 def _block_ranges(nblocks: int, parts: int):
     parts = max(1, min(parts, nblocks))
     step = -(-nblocks // parts)
@@ -493,13 +527,16 @@ def configs_bench(torch, z, K: int = 50) -> dict:
             torch.cuda.synchronize()
             ts = sorted(a.elapsed_time(b) for a, b in ev)
             ms = sum(ts) / K
+            del copies
+            cms = same_size_copy(torch, z, stream, rb + wb, K)
             out[name] = {"ms": round(ms, 5), "ms_p10": round(ts[int(0.1 * (K - 1))], 5),
                          "ms_p50": round(ts[(K - 1) // 2], 5), "ms_p90": round(ts[int(0.9 * (K - 1) + 0.5)], 5),
                          "in_GBps": round(rb / (ms * 1e-3) / 1e9, 1),
                          "hbm_frac": round((rb + wb) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                         "copy_same_size_ms": round(cms, 5), "of_copy_same_size": round(cms / ms, 4),
                          "copies": ncopy, "rotated_bytes": ncopy * nbytes(bufs)}
-            log(f"{name}: {ms * 1e3:.1f} us, {out[name]['hbm_frac']:.3f} of HBM peak ({ncopy} copies)")
-            del copies
+            log(f"{name}: {ms * 1e3:.1f} us, {out[name]['hbm_frac']:.3f} of HBM peak, "
+                f"{cms / ms:.3f} of a same-size copy ({ncopy} copies)")
         return out
 
     res = {}
@@ -771,6 +808,8 @@ def main() -> int:
     unfused = time_rows(torch, stream, step.unfused_launches(), step.unfused_kernels, K)
     extra = time_rows(torch, stream, step.extra_launches(), step.extra_kernels, K)
     copy = copy_ceiling(torch, z, stream, K)
+    # rows that move less than 1 GiB: also against a plain copy of their own size
+    same = {p[0]: same_size_copy(torch, z, stream, p[2] + p[3], K) for p in per if p[2] + p[3] < (1 << 30)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -805,7 +844,9 @@ def main() -> int:
         "kernels": {p[0]: {"ms": round(p[5], 5), **spread[p[0]], "in_GBps": round(p[2] / (p[5] * 1e-3) / 1e9, 1),
                            "rw_GBps": round((p[2] + p[3]) / (p[5] * 1e-3) / 1e9, 1),
                            "hbm_frac": round((p[2] + p[3]) / (p[5] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                           "copy_frac": round((p[2] + p[3]) / (p[5] * 1e-3) / 1e9 / copy["GBps"], 4)}
+                           "copy_frac": round((p[2] + p[3]) / (p[5] * 1e-3) / 1e9 / copy["GBps"], 4),
+                           **({"copy_same_size_ms": round(same[p[0]], 5),
+                               "of_copy_same_size": round(same[p[0]] / p[5], 4)} if p[0] in same else {})}
                     for p in per},
         "copy_ceiling": copy,
         "graph_step": {"ms_per_step": round(graph_ms, 4),
