@@ -96,6 +96,19 @@ namespace {
 #ifndef ZPP_DRR_LDS
 #define ZPP_DRR_LDS 1
 #endif
+// With 4-bit inputs and at most this many of them, the wide (LDS-staged)
+// layout is taken from ZPP_DRR_FEW_INPUTS_WAVES waves on, below the general
+// threshold: with few inputs the narrow layout's per-lane overhead (factors,
+// requantization per 8 elements) outweighs its extra waves once there are
+// about two wide waves per SIMD (measured on 2 or 4 inputs: at 1,953 waves
+// the wide layout 6-20% faster, at 976 waves 13% slower; with 8 inputs, or
+// 8-bit codes, no gain).
+#ifndef ZPP_DRR_FEW_INPUTS
+#define ZPP_DRR_FEW_INPUTS 4
+#endif
+#ifndef ZPP_DRR_FEW_INPUTS_WAVES
+#define ZPP_DRR_FEW_INPUTS_WAVES 1536
+#endif
 // Below this many waves of the wide layout, lanes take 8 elements each so
 // that small outputs still spread over every SIMD.
 #ifndef ZPP_DRR_NARROW_WAVES
@@ -728,7 +741,9 @@ hipError_t launch(const DrrArgs &a) {
     if constexpr (LOG2B >= 12) {
         return launch_e<BITS_IN, BITS_OUT, LOG2B, ZPP_DRR_WIDE_E, AVG>(a);
     } else {
-        if (wide_waves >= ZPP_DRR_NARROW_WAVES) return launch_e<BITS_IN, BITS_OUT, LOG2B, ZPP_DRR_WIDE_E, AVG>(a);
+        if (wide_waves >= ZPP_DRR_NARROW_WAVES ||
+            (BITS_IN == 4 && a.n_inputs <= ZPP_DRR_FEW_INPUTS && wide_waves >= ZPP_DRR_FEW_INPUTS_WAVES))
+            return launch_e<BITS_IN, BITS_OUT, LOG2B, ZPP_DRR_WIDE_E, AVG>(a);
         return launch_e<BITS_IN, BITS_OUT, LOG2B, 8, AVG>(a);
     }
 }

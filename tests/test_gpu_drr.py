@@ -19,6 +19,7 @@ import numpy as np
 import pytest
 
 import oracle
+import oracle_par
 import synth
 from gpu_util import Guarded, assert_bits_equal, assert_within_scale, dev, need_gpu, torch
 
@@ -209,6 +210,31 @@ def test_wide_lane_path(bits_in, bits_out, R, block):
     if bits_out:
         assert_bits_equal(gso, so, "scales (wide lanes)")
         assert_bits_equal(gco, co, "codes (wide lanes)")
+
+
+@pytest.mark.parametrize("R,bits_in,bits_out,waves", [(4, 4, 4, 1536), (4, 4, 4, 1535), (2, 4, 0, 1900),
+                                                       (1, 4, 4, 1600), (5, 4, 4, 1600), (4, 8, 8, 1600),
+                                                       (3, 4, 8, 2047)])
+def test_layout_choice_for_few_inputs(R, bits_in, bits_out, waves):
+    """With 4-bit codes and at most 4 inputs the 32-elements-per-lane layout
+    is taken from 1,536 waves of 2,048 elements on (below that, and with 5
+    inputs or 8-bit codes, the 8-element lanes up to 4,096 waves). Both sides
+    of that choice, each with a ragged last tile, against the oracle."""
+    block = 128
+    numel = (waves - 1) * 2048 + 7 * block
+    rng = np.random.default_rng([R, bits_in, waves])
+    per_c = numel * bits_in // 8
+    codes = rng.integers(0, 256, R * per_c, dtype=np.uint8)
+    scales = np.exp2(rng.uniform(-20, -5, R * (numel // block))).astype(np.float32)
+    gco, gso, gsu = _run(codes, per_c, scales, numel // block, R, bits_in, numel, block, bits_out)
+    cl = [codes[r * per_c:(r + 1) * per_c] for r in range(R)]
+    sl = [scales[r * (numel // block):(r + 1) * (numel // block)] for r in range(R)]
+    co, so, su = oracle_par.dequant_reduce_requant(cl, sl, bits_in, numel, block, bits_out)
+    what = f"R={R} bits={bits_in}->{bits_out} waves={waves}"
+    assert_bits_equal(gsu, su, "sum " + what)
+    if bits_out:
+        assert_bits_equal(gso, so, "scales " + what)
+        assert_bits_equal(gco, co, "codes " + what)
 
 
 # --------------------------------------------------------------------------
