@@ -261,9 +261,10 @@ struct Batch {
 
 // A lane's byte offsets within one input: of its code vectors and of their
 // block scales, the same for every input. An address is then a wave-uniform
-// base (input r's) plus a 32-bit lane offset, which the first batch of the
-// wide layout loads in the scalar-base form (global_load ... v_off, s[base]).
-// A launch covers at most 2^29 elements, so every offset fits in 32 bits.
+// base (input r's) plus a 32-bit lane offset: the LDS-staged layout hands the
+// two to its loads as a buffer resource and an offset, the register layouts
+// add them. A launch covers at most 2^29 elements, so every offset fits in
+// 32 bits.
 template <typename G>
 struct LaneOffsets {
     uint32_t code[G::U];
