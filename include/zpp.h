@@ -244,6 +244,9 @@ zpp_status zpp_dequant_reduce_requant(const void *codes_in, int64_t codes_stride
  *                     (both may be NULL when keep_elems == 0)
  *   bits_out     in   8 or 4
  *   stream       in   hipStream_t
+ * Errors as zpp_dequant_reduce_requant's, and ZPP_ERR_ARG for a window that
+ * is not whole blocks or does not lie inside [0, numel); ZPP_ERR_OVERLAP
+ * when any two of the four outputs overlap.
  */
 zpp_status zpp_dequant_reduce_requant_split(const void *codes_in, int64_t codes_stride_bytes,
                                             const float *scales_in, int64_t scales_stride,
