@@ -195,3 +195,65 @@ def test_random_hop_reduce_and_average(seed):
     assert ga.untouched()
     assert_bits_equal(ga.as_np(np.float32), oracle.dequant_average(cl, sl, bits_in, n, B, divisor),
                       f"average seed={seed} divisor={divisor}")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_wide_hops(seed):
+    """Random hops large enough for the 32-elements-per-lane layouts: the
+    LDS-staged one (4-bit inputs, blocks up to 2048; from 1,536 waves with at
+    most 4 inputs, else from 4,096) and the register one (8-bit inputs, and
+    4,096-element blocks), with random input counts, strides with gaps, code
+    bytes, scales across binades and a random kept window for the split."""
+    import oracle_par
+    z = _z()
+    rng = np.random.default_rng([603, seed])
+    bits_in = int(rng.choice([4, 4, 8]))
+    B = int(rng.choice([32, 128, 256, 512, 2048, 4096]))
+    R = int(rng.integers(1, 13))
+    waves = int(rng.integers(1536 if (bits_in == 4 and R <= 4) else 4096, 4600))
+    n = (waves * 2048 - int(rng.integers(0, 2048))) // B * B
+    bits_out = int(rng.choice([4, 8]))
+    gap_blocks = int(rng.integers(0, 3))
+    per_c = (n + gap_blocks * B) * bits_in // 8
+    per_c += (-per_c) % 16
+    per_s = n // B + gap_blocks
+    codes = rng.integers(0, 256, R * per_c, dtype=np.uint8)
+    scales = np.exp2(rng.uniform(-30, 10, R * per_s)).astype(np.float32)
+    scales[rng.random(scales.size) < 0.02] = 0.0
+    cl = [codes[r * per_c:r * per_c + n * bits_in // 8] for r in range(R)]
+    sl = [scales[r * per_s:r * per_s + n // B] for r in range(R)]
+    cd, sd = dev(codes), dev(scales)
+    co, so, su = oracle_par.dequant_reduce_requant(cl, sl, bits_in, n, B, bits_out)
+    what = f"seed={seed} B={B} R={R} n={n} {bits_in}->{bits_out}"
+    gc, gs, gu = Guarded(n * bits_out // 8), Guarded(4 * (n // B)), Guarded(4 * n)
+    torch.cuda.synchronize()
+    z.zpp_dequant_reduce_requant(cd, per_c, sd, per_s, R, bits_in, n, B, gc.ptr, gs.ptr, bits_out, gu.ptr)
+    torch.cuda.synchronize()
+    assert gc.untouched() and gs.untouched() and gu.untouched()
+    assert_bits_equal(gu.as_np(np.float32), su, "sum " + what)
+    assert_bits_equal(gs.as_np(np.float32), so, "scales " + what)
+    assert_bits_equal(gc.bytes(), co, "codes " + what)
+    nb = n // B
+    k0 = int(rng.integers(0, nb + 1))
+    kl = int(rng.integers(0, nb - k0 + 1))
+    k0, kl = k0 * B, kl * B
+    gsc = Guarded((n - kl) * bits_out // 8) if n > kl else None
+    gss = Guarded(4 * ((n - kl) // B)) if n > kl else None
+    gkc = Guarded(kl * bits_out // 8) if kl else None
+    gks = Guarded(4 * (kl // B)) if kl else None
+    torch.cuda.synchronize()
+    z.zpp_dequant_reduce_requant_split(cd, per_c, sd, per_s, R, bits_in, n, B, k0, kl,
+                                       gsc.ptr if gsc else None, gss.ptr if gss else None,
+                                       gkc.ptr if gkc else None, gks.ptr if gks else None, bits_out)
+    torch.cuda.synchronize()
+    cb = bits_out / 8
+    c0, c1 = int(k0 * cb), int((k0 + kl) * cb)
+    if kl:
+        assert gkc.untouched() and gks.untouched()
+        assert_bits_equal(gkc.bytes(), co[c0:c1], "split kept codes " + what)
+        assert_bits_equal(gks.as_np(np.float32), so[k0 // B:(k0 + kl) // B], "split kept scales " + what)
+    if n > kl:
+        assert gsc.untouched() and gss.untouched()
+        assert_bits_equal(gsc.bytes(), np.concatenate([co[:c0], co[c1:]]), "split sent codes " + what)
+        assert_bits_equal(gss.as_np(np.float32), np.concatenate([so[:k0 // B], so[(k0 + kl) // B:]]),
+                          "split sent scales " + what)
