@@ -197,7 +197,7 @@ def test_random_hop_reduce_and_average(seed):
                       f"average seed={seed} divisor={divisor}")
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(16))
 def test_random_wide_hops(seed):
     """Random hops large enough for the 32-elements-per-lane layouts: the
     LDS-staged one (4-bit inputs, blocks up to 2048; from 1,536 waves with at
