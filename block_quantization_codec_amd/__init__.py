@@ -272,6 +272,30 @@ def dequant_reduce_requant(codes_in, scales_in, n_inputs: int, bits_in: int, num
     return co, so, su
 
 
+def dequant_reduce_requant_split(codes_in, scales_in, n_inputs: int, bits_in: int, numel: int, block: int,
+                                 keep_begin: int, keep_elems: int, bits_out: int,
+                                 codes_stride_bytes: int | None = None, scales_stride: int | None = None,
+                                 stream=None):
+    """The requantized sum of ``n_inputs`` pieces split in one pass: elements
+    [keep_begin, keep_begin + keep_elems) (whole blocks) to the kept pair, all
+    others, in order, to the send pair. Returns (send_codes, send_scales,
+    keep_codes, keep_scales), with None for an empty pair."""
+    import torch
+
+    _need_contiguous(codes_in=codes_in, scales_in=scales_in)
+    dev = codes_in.device
+    cs = codes_stride_bytes if codes_stride_bytes is not None else numel * bits_in // 8
+    ss = scales_stride if scales_stride is not None else numel // block
+    send = numel - keep_elems
+    sc = torch.empty(send * bits_out // 8, dtype=torch.uint8, device=dev) if send > 0 else None
+    sS = torch.empty(send // block, dtype=torch.float32, device=dev) if send > 0 else None
+    kc = torch.empty(keep_elems * bits_out // 8, dtype=torch.uint8, device=dev) if keep_elems > 0 else None
+    kS = torch.empty(keep_elems // block, dtype=torch.float32, device=dev) if keep_elems > 0 else None
+    zpp_dequant_reduce_requant_split(codes_in, cs, scales_in, ss, n_inputs, bits_in, numel, block, keep_begin,
+                                     keep_elems, sc, sS, kc, kS, bits_out, stream)
+    return sc, sS, kc, kS
+
+
 def dequant_reduce_average(codes_in, scales_in, n_inputs: int, bits_in: int, numel: int, block: int, divisor: int,
                            codes_stride_bytes: int | None = None, scales_stride: int | None = None, stream=None):
     """Sum ``n_inputs`` quantized pieces laid side by side and divide by ``divisor``

@@ -173,3 +173,28 @@ def test_split_matches_the_unsplit_call_on_random_code_bytes():
     co, so, _ = oracle.dequant_reduce_requant(list(cl), list(sl), 4, numel, B, 4)
     assert_bits_equal(fc, co, "unsplit codes vs oracle")
     assert_bits_equal(fs, so, "unsplit scales vs oracle")
+
+
+def test_tensor_helper_matches_the_raw_entry_point():
+    """block_quantization_codec_amd.dequant_reduce_requant_split (outputs
+    allocated by the binding) equals the oracle's requantized sum, cut at the
+    window, for a hop of 8 inputs and for a window covering everything."""
+    import block_quantization_codec_amd as z
+    R, B = 8, 256
+    numel = 4096 * 2048 + 5 * B
+    codes, pc, scales, ps = _inputs(R, 4, numel, B, 31, random_bytes=True)
+    cl = [codes[r * pc:(r + 1) * pc] for r in range(R)]
+    sl = [scales[r * ps:(r + 1) * ps] for r in range(R)]
+    co, so, _ = oracle_par.dequant_reduce_requant(cl, sl, 4, numel, B, 4)
+    cd, sd = dev(codes), dev(scales)
+    for k0, kl in ((777 * B, 1953 * B), (0, numel)):
+        sc, ss, kc, ks = z.dequant_reduce_requant_split(cd, sd, R, 4, numel, B, k0, kl, 4)
+        torch.cuda.synchronize()
+        c0, c1 = k0 // 2, (k0 + kl) // 2
+        assert_bits_equal(kc.cpu().numpy(), co[c0:c1], "keep codes")
+        assert_bits_equal(ks.cpu().numpy(), so[k0 // B:(k0 + kl) // B], "keep scales")
+        if kl < numel:
+            assert_bits_equal(sc.cpu().numpy(), np.concatenate([co[:c0], co[c1:]]), "send codes")
+            assert_bits_equal(ss.cpu().numpy(), np.concatenate([so[:k0 // B], so[(k0 + kl) // B:]]), "send scales")
+        else:
+            assert sc is None and ss is None
