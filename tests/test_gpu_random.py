@@ -257,3 +257,47 @@ def test_random_wide_hops(seed):
         assert_bits_equal(gsc.bytes(), np.concatenate([co[:c0], co[c1:]]), "split sent codes " + what)
         assert_bits_equal(gss.as_np(np.float32), np.concatenate([so[:k0 // B], so[(k0 + kl) // B:]]),
                           "split sent scales " + what)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_wide_sums(seed):
+    """Random hops of the 32-elements-per-lane layouts that write only binary32
+    sums or averages (the last hop), whose sums go out through LDS so that each
+    store is contiguous across the wave: the LDS-staged layout (4-bit inputs,
+    blocks up to 2048) reuses its code slots for them, the register layout
+    (8-bit inputs, 4,096-element blocks) has its own. Random input counts,
+    strides with gaps, scales across binades, a ragged end, random divisors."""
+    import oracle_par
+    z = _z()
+    rng = np.random.default_rng([604, seed])
+    bits_in = int(rng.choice([4, 8]))
+    B = int(rng.choice([32, 128, 256, 1024, 2048, 4096]))
+    R = int(rng.integers(1, 40))
+    waves = int(rng.integers(1536 if (bits_in == 4 and R <= 4) else 4096, 4600))
+    n = (waves * 2048 - int(rng.integers(0, 2048))) // B * B
+    gap_blocks = int(rng.integers(0, 3))
+    per_c = (n + gap_blocks * B) * bits_in // 8
+    per_c += (-per_c) % 16
+    per_s = n // B + gap_blocks
+    codes = rng.integers(0, 256, R * per_c, dtype=np.uint8)
+    scales = np.exp2(rng.uniform(-30, 10, R * per_s)).astype(np.float32)
+    scales[rng.random(scales.size) < 0.02] = 0.0
+    cl = [codes[r * per_c:r * per_c + n * bits_in // 8] for r in range(R)]
+    sl = [scales[r * per_s:r * per_s + n // B] for r in range(R)]
+    cd, sd = dev(codes), dev(scales)
+    what = f"seed={seed} B={B} R={R} n={n} bits={bits_in}"
+    _, _, su = oracle_par.dequant_reduce_requant(cl, sl, bits_in, n, B, 0)
+    gu = Guarded(4 * n)
+    torch.cuda.synchronize()
+    z.zpp_dequant_reduce_requant(cd, per_c, sd, per_s, R, bits_in, n, B, None, None, 0, gu.ptr)
+    torch.cuda.synchronize()
+    assert gu.untouched()
+    assert_bits_equal(gu.as_np(np.float32), su, "sum " + what)
+    divisor = int(rng.choice([3, 7, 96, 256, 1 << 20]))
+    ga = Guarded(4 * n)
+    torch.cuda.synchronize()
+    z.zpp_dequant_reduce_average(cd, per_c, sd, per_s, R, bits_in, n, B, divisor, ga.ptr)
+    torch.cuda.synchronize()
+    assert ga.untouched()
+    assert_bits_equal(ga.as_np(np.float32), oracle.dequant_average(cl, sl, bits_in, n, B, divisor),
+                      f"average {what} divisor={divisor}")
