@@ -533,6 +533,7 @@ def configs_bench(torch, z, K: int = 50) -> dict:
                          "ms_p50": round(ts[(K - 1) // 2], 5), "ms_p90": round(ts[int(0.9 * (K - 1) + 0.5)], 5),
                          "in_GBps": round(rb / (ms * 1e-3) / 1e9, 1),
                          "hbm_frac": round((rb + wb) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                         "rw_bytes": rb + wb,
                          "copy_same_size_ms": round(cms, 5), "of_copy_same_size": round(cms / ms, 4),
                          "copies": ncopy, "rotated_bytes": ncopy * nbytes(bufs)}
             log(f"{name}: {ms * 1e3:.1f} us, {out[name]['hbm_frac']:.3f} of HBM peak, "
@@ -598,7 +599,18 @@ def configs_bench(torch, z, K: int = 50) -> dict:
          w1, C // 2 + 4 * C // B2),
         ("hop1_4way_all_8_shares", (q2c, q2s, h2c, h2s), hop1_all, N * w1, N * (C // 2 + 4 * C // B2)),
     ])
-    del grads, reord, q2c, q2s, h2c, h2s, sh_c, sh_s, o1c, o1s
+    # hop 2 of the same grid for one GPU (node n-1, local rank g-1): its slice
+    # of both nodes' hop-1 outputs (filled by the hop-1 row above), summed in
+    # binary32
+    off2 = (g - 1) * C + (n - 1) * S
+    o2 = torch.empty(S, dtype=torch.float32, device=dev)
+    res[c2.name].update(rows([
+        ("hop2_2way_one_shard_fp32", (h2c, h2s, o2),
+         lambda b: z.zpp_dequant_reduce_requant(b[0][off2 // 2:], P // 2, b[1][off2 // B2:], P // B2, n, 4, S, B2,
+                                                None, None, 0, b[2]),
+         n * (S // 2 + 4 * S // B2), 4 * S),
+    ]))
+    del grads, reord, q2c, q2s, h2c, h2s, sh_c, sh_s, o1c, o1s, o2
     # 64 int8 shards (block 2048) of a Llama-style layer, dequantized in one launch
     c3 = synth.QWZ_DEQUANT_64
     n3, B3 = c3.numel, c3.block
@@ -612,6 +624,13 @@ def configs_bench(torch, z, K: int = 50) -> dict:
         ("dequantize_int8_b2048_64_shards", (q3c, q3s, y3),
          lambda b: z.zpp_dequantize_blocks(b[0], b[1], 8, n3, B3, b[2], z.ZPP_BF16), n3 + 4 * n3 // B3, 2 * n3),
     ])
+    del y3
+    # the same codes to binary32 (a full-precision copy of the weights)
+    y3f = torch.empty(n3, dtype=torch.float32, device=dev)
+    res[c3.name].update(rows([
+        ("dequantize_int8_b2048_64_shards_f32", (q3c, q3s, y3f),
+         lambda b: z.zpp_dequantize_blocks(b[0], b[1], 8, n3, B3, b[2], z.ZPP_FP32), n3 + 4 * n3 // B3, 4 * n3),
+    ]))
     return res
 
 

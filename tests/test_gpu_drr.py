@@ -92,9 +92,12 @@ def _check(R, bits_in, bits_out, block, numel, seed, gap=0, want_sum=True):
         assert_bits_equal(gco, co, "codes " + what)
 
 
-@pytest.mark.parametrize("R", [1, 2, 3, 4, 5, 8, 9, 32, 33])
+@pytest.mark.parametrize("R", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 15, 32, 33, 34, 35])
 @pytest.mark.parametrize("bits_in,bits_out", [(4, 4), (8, 8), (4, 0)])
 def test_input_counts(R, bits_in, bits_out):
+    """Every way the 8-elements-per-lane layout splits its inputs: batches of
+    8 (the next one loading while the last is summed), then of 4, then the
+    last 1, 2 or 3 as one batch."""
     _check(R, bits_in, bits_out, 256, 256 * 100, 1)
 
 
