@@ -33,10 +33,6 @@ constexpr int kSeg = kWave * kE;   // 512
 #ifndef ZPP_DEQUANT_SEGS_F32
 #define ZPP_DEQUANT_SEGS_F32 1
 #endif
-// 1: binary32 output in the split-half lane layout
-#ifndef ZPP_DEQUANT_F32_SPLIT
-#define ZPP_DEQUANT_F32_SPLIT 1
-#endif
 // segments per tile
 template <int BITS, bool F32OUT>
 constexpr int segs() { return F32OUT ? ZPP_DEQUANT_SEGS_F32 : (BITS == 8 ? ZPP_DEQUANT_SEGS8 : ZPP_DEQUANT_SEGS4); }
@@ -54,7 +50,7 @@ __global__ __launch_bounds__(kBlockThreads) void dequantize_kernel(const uint8_t
     constexpr int kTile = tile<BITS, F32OUT>();
 
     for (int64_t t0 = wave * kTile; t0 < numel; t0 += n_waves * kTile) {
-        if constexpr (F32OUT && ZPP_DEQUANT_F32_SPLIT) {
+        if constexpr (F32OUT) {
             // binary32 out: the lane takes 4 elements from each half of the segment, so
             // each 16-byte store covers 1 KB that is contiguous across the wave
             constexpr int kH = kSeg / 2;
@@ -88,6 +84,7 @@ __global__ __launch_bounds__(kBlockThreads) void dequantize_kernel(const uint8_t
                 }
             }
         } else {
+            // bf16 out: 8 consecutive elements per lane and segment
             uint32_t w[kU][2];
             float s[kU];
             bool ok[kU];
@@ -116,14 +113,8 @@ __global__ __launch_bounds__(kBlockThreads) void dequantize_kernel(const uint8_t
                     const int32_t q = (BITS == 8) ? code_at<8>(w[u][i / 4], i % 4) : code_at<4>(w[u][0], i);
                     f[i] = static_cast<float>(q) * s[u];
                 }
-                if constexpr (F32OUT) {
-                    uint8_t *dst = y + e0 * 4;
-                    st_out<u32x4>(dst, u32x4{as_u(f[0]), as_u(f[1]), as_u(f[2]), as_u(f[3])});
-                    st_out<u32x4>(dst + 16, u32x4{as_u(f[4]), as_u(f[5]), as_u(f[6]), as_u(f[7])});
-                } else {
-                    st_out<u32x4>(y + e0 * 2, u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
-                                                pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])});
-                }
+                st_out<u32x4>(y + e0 * 2, u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                                            pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])});
             }
         }
     }
