@@ -75,7 +75,13 @@ def test_quantize_and_dequantize_past_2_31(x, bits, block):
     assert_bits_equal(host(scales)[idx], os_, f"int{bits} scales")
     oy = oracle.dequantize(oc, os_, bits, xs.size, block, out="bf16")
     assert_bits_equal(_gather_rows(y, block, idx), oy, f"int{bits} dequantized bf16")
-    del codes, scales, y
+    del y
+    # binary32 out: 8.7 GB, byte offsets past 2^33 (read back with slice copies)
+    yf = z.dequantize(codes, scales, bits, N, block, dtype=torch.float32)
+    torch.cuda.synchronize()
+    of = oracle.dequantize(oc, os_, bits, xs.size, block, out="f32")
+    assert_bits_equal(_rows_by_copies(yf, block, idx), of, f"int{bits} dequantized binary32")
+    del codes, scales, yf
 
 
 def test_reorder_and_fused_quantize_past_2_31(x):
