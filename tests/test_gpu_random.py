@@ -56,7 +56,7 @@ def _scales(rng, n: int) -> np.ndarray:
     return s
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(96))
 def test_random_quantize_and_dequantize(seed):
     z = _z()
     rng = np.random.default_rng([600, seed])
@@ -88,7 +88,7 @@ def test_random_quantize_and_dequantize(seed):
     assert_bits_equal(gy.as_np(np.float32 if out_f32 else np.uint16), oy, f"dequantized seed={seed}")
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(48))
 def test_random_reorder_and_fused_quantize(seed):
     z = _z()
     rng = np.random.default_rng([601, seed])
@@ -121,7 +121,7 @@ def test_random_reorder_and_fused_quantize(seed):
     assert_bits_equal(gs.as_np(np.float32), os_, f"fused scales seed={seed}")
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(96))
 def test_random_hop_reduce_and_average(seed):
     z = _z()
     rng = np.random.default_rng([602, seed])
@@ -197,7 +197,7 @@ def test_random_hop_reduce_and_average(seed):
                       f"average seed={seed} divisor={divisor}")
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(24))
 def test_random_wide_hops(seed):
     """Random hops large enough for the 32-elements-per-lane layouts: the
     LDS-staged one (4-bit inputs, blocks up to 2048; from 1,536 waves with at
@@ -259,7 +259,7 @@ def test_random_wide_hops(seed):
                           "split sent scales " + what)
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(16))
 def test_random_wide_sums(seed):
     """Random hops of the 32-elements-per-lane layouts that write only binary32
     sums or averages (the last hop), whose sums go out through LDS so that each
